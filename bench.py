@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Throughput of the paged decode path on one MI355X.
+
+Workload: the Llama-7B-shaped single-layer decode batch (96 sequences, 32 heads x
+128, block size 16, contexts uniform in [300, 2048], fp16 KV and q, fp32
+accumulation, blocks scattered at random over a pool of 110% of the blocks needed).
+
+One step = one pass of the hot path over that batch: the slot-mapped append of
+each sequence's newest K/V row (pa_cache_append, 96 rows) followed by pa_decode
+(partition pass + reduce pass).  The slot mapping is computed on the host before
+the timed region; the batch has no shared blocks, so no block copy is due.
+
+Printed: one JSON line.  value = decode KV bytes per step / time per step (GB/s),
+with every input resident in HBM.  roofline: the partition pass (the dominant
+kernel) timed alone with HIP events on the stream it runs on; achieved = its
+algorithmic bytes (live K and V rows) / its average duration, against 8 TB/s.
+cpu_baseline: the CPU oracle on a bounded sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--partition", type=int, default=0, help="tokens per partition, 0 = auto")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, msg):
+    if not args.quiet:
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_launches(fn, n, torch):
+    """Average ms of ``fn`` over n back-to-back launches, HIP events on the current
+    stream (the stream every entry point here launches on)."""
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / n
+
+
+def cpu_baseline(batch, budget_s):
+    """The oracle as it stands, single-threaded BLAS, over (seq, head) pairs in order
+    until the time budget is spent."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    from paged_kv_cache_414_amd import metrics
+
+    h_count = batch.num_heads
+    done_tokens = 0
+    pairs = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for s in range(batch.num_seqs):
+            for h in range(h_count):
+                oracle.decode_one(batch.q[s, h], batch.k_pool, batch.v_pool,
+                                  batch.block_tables[s], batch.context_lens[s], h, batch.scale)
+                done_tokens += int(batch.context_lens[s])
+                pairs += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            else:
+                continue
+            break
+        elapsed = time.perf_counter() - t0
+    nbytes = metrics.kv_bytes_per_token(1, 1, batch.head_dim, batch.q.itemsize) * done_tokens
+    return {
+        "value": round(metrics.gbps(nbytes, elapsed), 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {pairs} (seq, head) pairs of the batch in order "
+                   f"({done_tokens} tokens, {elapsed:.1f} s), fp64 numpy, BLAS limited to 1 thread"),
+        "seq_steps_per_s": round(pairs / h_count / elapsed, 4),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence or head with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_414_amd import blocks, metrics, ops, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    log(args, "generating the llama7b_decode batch")
+    batch = workloads.llama7b_decode(seed=args.seed, poison=False)
+    s_count, h_count, d = batch.q.shape
+    bs = batch.block_size
+    ctx = batch.context_lens
+    max_ctx = batch.max_context_len
+    positions = ctx.astype(np.int64) - 1  # each sequence's newest token
+    slots = blocks.slots_for_positions(batch.block_tables, positions, bs)
+    rng = np.random.default_rng([args.seed, 7])
+    new_k = workloads.normal(rng, (s_count, h_count, d), batch.dtype)
+    new_v = workloads.normal(rng, (s_count, h_count, d), batch.dtype)
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    q, kc, vc = dev(batch.q), dev(batch.k_pool), dev(batch.v_pool)
+    tables, ctx_d, slots_d = dev(batch.block_tables), dev(ctx), dev(slots)
+    nk, nv = dev(new_k), dev(new_v)
+    out = torch.empty_like(q)
+    part = ops.pa_decode_partition_size(s_count, h_count, bs, max_ctx, args.partition)
+    n_parts = ops.pa_decode_num_partitions(s_count, h_count, bs, max_ctx, args.partition)
+    ws = ops.workspace_for(q, kc, max_ctx, args.partition)
+
+    def step():
+        ops.pa_cache_append(kc, vc, nk, nv, slots_d)
+        ops.pa_decode(out, q, kc, vc, tables, ctx_d, batch.scale, max_ctx, args.partition, ws)
+
+    def partitions_only():
+        ops.pa_decode_partitions(out, q, kc, vc, tables, ctx_d, batch.scale, max_ctx,
+                                 args.partition, ws)
+
+    def decode_only():
+        ops.pa_decode(out, q, kc, vc, tables, ctx_d, batch.scale, max_ctx, args.partition, ws)
+
+    log(args, f"warmup {args.warmup} steps (P={part}, NP={n_parts})")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(args, f"timing {args.steps} steps")
+    ms_step = time_launches(step, args.steps, torch)
+    log(args, "timing the partition pass alone")
+    for _ in range(args.warmup):
+        partitions_only()
+    ms_part = time_launches(partitions_only, args.steps, torch)
+    ms_decode = time_launches(decode_only, args.steps, torch)
+
+    kv = metrics.decode_kv_bytes(ctx, h_count, d, batch.q.itemsize)
+    value = metrics.gbps(kv, ms_step * 1e-3)
+    achieved = metrics.gbps(kv, ms_part * 1e-3)
+    record = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama7b_decode",
+            "num_seqs": s_count, "num_heads": h_count, "head_dim": d, "block_size": bs,
+            "context_lens": "uniform [300, 2048]", "sum_context": int(ctx.sum()),
+            "max_context": max_ctx, "num_blocks": batch.num_blocks,
+            "partition_tokens": part, "num_partitions": n_parts, "seed": args.seed,
+            "step": "pa_cache_append (96 rows) + pa_decode",
+        },
+        "pct_of_hbm_peak": round(100.0 * value / metrics.HBM_PEAK_GBPS, 2),
+        "seq_steps_per_s": round(s_count / (ms_step * 1e-3), 1),
+        "decode_ms": round(ms_decode, 5),
+        "decode_kv_gbps": round(metrics.gbps(kv, ms_decode * 1e-3), 2),
+        "kv_bytes_per_step": kv,
+        "roofline": {
+            "kernel": "decode_partitions_kernel<f16, 128, 16>",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": metrics.HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / metrics.HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_ms": round(ms_part, 5),
+            "algorithmic_bytes_per_launch": kv,
+        },
+    }
+    if args.cpu_seconds > 0:
+        log(args, f"CPU oracle baseline ({args.cpu_seconds:.0f} s budget)")
+        record["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+    else:
+        record["cpu_baseline"] = None
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

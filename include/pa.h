@@ -1,0 +1,222 @@
+/*
+ * pa.h -- C ABI of the paged KV-cache decode path for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, then section):
+ *   [Reading vLLM]  "啃透vLLM源码：从PagedAttention到连续批处理，大模型推理加速24倍的秘密"
+ *                   (Reading the vLLM source: from PagedAttention to continuous batching)
+ *   [vLLM basics]   "vLLM基础：架构、推理流程与关键组件"
+ *                   (vLLM basics: architecture, inference flow and key components)
+ *   [vLLM analysis] "VLLM源码解析：高效大规模语言模型推理的技术实现"
+ *                   (vLLM source analysis: technical implementation of efficient inference)
+ *
+ * The method: each sequence's KV cache is cut into fixed-size blocks (16 tokens by
+ * default) that may sit anywhere in a physical pool; a per-sequence block table maps
+ * logical block i to its physical block ([Reading vLLM] §2.2; [vLLM basics] §2.3).
+ * Attention for the newest token reads the query, the key and value caches and the
+ * physical block indices ([vLLM analysis], design principles).  Blocks are shared
+ * by reference count and copied before a sharer writes ([Reading vLLM] §2.2;
+ * [vLLM basics] §2.3, copy-on-write).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  * Every array pointer is a DEVICE pointer owned by the caller.  The library keeps
+ *    no pointer after a call returns and allocates no device memory.
+ *  * All arrays are dense, row-major (C order) and 16-byte aligned.
+ *  * `stream` is a hipStream_t (NULL = the legacy default stream).  Each call only
+ *    enqueues work on it and returns without waiting; ordering between calls comes
+ *    from stream order.
+ *  * Element type: PA_F32 (float) or PA_F16 (IEEE binary16).  The query, both pools,
+ *    the appended key/value rows and the output share one element type.
+ *  * Layouts:
+ *      query, out            [num_seqs, num_heads, head_dim]
+ *      key, value (append)   [num_tokens, num_heads, head_dim]
+ *      key_cache, value_cache[num_blocks, num_heads, block_size, head_dim]
+ *      block_tables          int32 [num_seqs, max_blocks_per_seq]; row s entry i is
+ *                            the physical block of logical block i of sequence s.
+ *                            Entries at i >= ceil(context_lens[s] / block_size) are
+ *                            never read for addressing and may hold any value.
+ *      context_lens          int32 [num_seqs], tokens of each sequence, >= 0.
+ *      slot_mapping          int32 [num_tokens]; slot = block * block_size + offset.
+ *                            A negative slot means "skip this row".
+ *      block_pairs           int32 [num_pairs, 2] = (source block, destination block).
+ *  * Supported shapes: head_dim in {64, 128}; block_size in {8, 16, 32};
+ *    other values return PA_ERR_UNSUPPORTED.  K/V heads equal query heads.
+ *  * Errors: argument checks run on the host before anything is enqueued and return
+ *    a status; nothing aborts and no C++ exception crosses the ABI.  A failed launch
+ *    returns PA_ERR_HIP.  The text of the last error of the calling thread is
+ *    available from pa_last_error().
+ *  * Device-side contents are caller preconditions and are not checked: block ids in
+ *    [0, num_blocks) for every live logical block, context_lens[s] <=
+ *    min(max_context_len, max_blocks_per_seq * block_size), distinct non-negative
+ *    slots below num_blocks * block_size, and copy pairs whose destinations are
+ *    distinct and never a source.  Violations are undefined behaviour.
+ *  * Concurrent calls from several host threads are safe; calls that write the same
+ *    memory must be ordered by the caller (same stream or events).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,          /* a required pointer is NULL */
+  PA_ERR_INVALID_ARG = 2,   /* a size or value is out of range or inconsistent */
+  PA_ERR_UNSUPPORTED = 3,   /* dtype, head_dim or block_size not built */
+  PA_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required */
+  PA_ERR_HIP = 5            /* the HIP runtime reported an error */
+} pa_status;
+
+/* Version of this ABI (PA_ABI_VERSION of the library that was built). */
+int32_t pa_abi_version(void);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pa_status_string(pa_status status);
+
+/* Message describing the last failing call made by this host thread, or "" if none
+ * failed.  Static thread-local storage: valid until the thread's next call. */
+const char* pa_last_error(void);
+
+/*
+ * Split-context planning.
+ *
+ * Decode attention of a sequence is computed over partitions of `partition_size`
+ * consecutive tokens; each partition yields a partial softmax state that a second
+ * pass merges by the log-sum-exp rule (Milakov & Gimelshein 2018, "Online
+ * normalizer calculation for softmax").  This splitting is this library's own way
+ * of spreading long contexts over the GPU; the pages state only the result, which
+ * equals attention over the whole sequence.
+ *
+ * pa_decode_partition_size returns the partition length (tokens) that pa_decode
+ * uses for these arguments: `partition_size` itself when it is > 0 (it must then be
+ * a positive multiple of block_size), otherwise the library's choice.  The value
+ * is always a multiple of block_size.  Returns -1 for invalid arguments.
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads,
+                                 int32_t block_size, int32_t max_context_len,
+                                 int32_t partition_size);
+
+/* Number of partitions per (sequence, head) reserved in the workspace:
+ * ceil(max_context_len / P) with P = pa_decode_partition_size(...), at least 1.
+ * Returns -1 for invalid arguments. */
+int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_heads,
+                                 int32_t block_size, int32_t max_context_len,
+                                 int32_t partition_size);
+
+/*
+ * Bytes of workspace pa_decode needs; 0 when every sequence fits one partition
+ * (the workspace pointer may then be NULL).  Layout, with NP =
+ * pa_decode_num_partitions(...), all float32:
+ *     m [num_seqs, num_heads, NP]   at byte 0
+ *     l [num_seqs, num_heads, NP]   at byte ws_align(S*H*NP*4)
+ *     o [num_seqs, num_heads, NP, head_dim]   at byte 2*ws_align(S*H*NP*4)
+ * where ws_align rounds up to 256.  For partition p of (s, h) over its tokens t:
+ *     m = max_t z_t,  l = sum_t 2^(z_t - m),  o = sum_t 2^(z_t - m) * v_t,
+ *     z_t = scale * log2(e) * <q, k_t>
+ * (base-2 logits).  Returns 0 and sets the last error for invalid arguments.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode -- single-query paged attention ([vLLM analysis], design principles:
+ * attention over query, key_cache, value_cache and the physical block indices).
+ *
+ * For every sequence s and head h, with L = context_lens[s]:
+ *     k_t = key_cache[block_tables[s][t / bs], h, t % bs, :]  (likewise v_t), t < L
+ *     out[s, h, :] = sum_t softmax_t(scale * <query[s, h, :], k_t>) * v_t
+ * and out[s, h, :] = 0 when L = 0.  Arithmetic is float32 (products, softmax,
+ * accumulation); the result is rounded once to the element type.
+ *
+ * max_context_len must be >= every context_lens[s] and <= max_blocks_per_seq *
+ * block_size; it sizes the grid.  partition_size: 0 = library choice, else a positive
+ * multiple of block_size.  workspace: device memory of at least
+ * pa_decode_workspace_bytes(...) bytes (may be NULL if that is 0); its contents on
+ * entry do not matter and on return are the partition states described above.
+ * Enqueues pa_decode_partitions and, when more than one partition is reserved,
+ * pa_decode_reduce.
+ */
+pa_status pa_decode(void* out, const void* query, const void* key_cache,
+                    const void* value_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                    pa_dtype dtype, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_partitions -- first pass of pa_decode alone (same arguments).
+ * Sequences with L <= P get their final output written to `out`; for the others,
+ * every partition p < ceil(L / P) writes its (m, l, o) state to the workspace and
+ * `out` is left for pa_decode_reduce.  Exposed so the two passes can be timed and
+ * checked separately.
+ */
+pa_status pa_decode_partitions(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_context_len, float scale, pa_dtype dtype,
+                               int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_reduce -- second pass: for every (s, h) with ceil(L / P) > 1, merge the
+ * partition states in the workspace:
+ *     M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
+ * rounded once to the element type.  Other sequences' outputs are not touched.
+ * block_size, max_context_len and partition_size must be those given to
+ * pa_decode_partitions.
+ */
+pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_context_len, pa_dtype dtype,
+                           int32_t partition_size, void* stream);
+
+/*
+ * pa_cache_append -- write each step's new K/V rows into the slots their positions
+ * map to (blocks fill slot by slot: [Reading vLLM] §2.2, LogicalTokenBlock).
+ * For i < num_tokens with slot = slot_mapping[i] >= 0, b = slot / block_size,
+ * o = slot % block_size, and every head h:
+ *     key_cache[b, h, o, :] = key[i, h, :];  value_cache[b, h, o, :] = value[i, h, :]
+ * Bits are copied unchanged.  Rows with a negative slot are skipped.  Slots must be
+ * distinct (caller precondition).
+ */
+pa_status pa_cache_append(void* key_cache, void* value_cache, const void* key,
+                          const void* value, const int32_t* slot_mapping,
+                          int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                          void* stream);
+
+/*
+ * pa_block_copy -- the copy-on-write duplication: when sequences that share a block
+ * diverge, the writer first gets its own copy ([vLLM basics] §2.3, copy-on-write;
+ * [Reading vLLM] §2.2, ref_count).  For each pair (src, dst):
+ *     key_cache[dst] = key_cache[src];  value_cache[dst] = value_cache[src]
+ * (all heads, all slots, bits unchanged).  Destinations must be distinct and never
+ * a source (caller precondition), so the pairs may run in any order.
+ */
+pa_status pa_block_copy(void* key_cache, void* value_cache, const int32_t* block_pairs,
+                        int32_t num_pairs, int32_t num_heads, int32_t head_dim,
+                        int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                        void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* PA_H_ */

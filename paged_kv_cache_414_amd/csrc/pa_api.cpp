@@ -1,0 +1,320 @@
+// C ABI of the paged KV-cache decode path: argument checks, planning of the
+// split-context pass, dispatch to the HIP kernels and error reporting.
+// The contract of every entry point is documented in include/pa.h.
+
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "pa_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pa_status ok() {
+  g_last_error[0] = '\0';
+  return PA_OK;
+}
+
+pa_status from_hip(hipError_t err, const char* what) {
+  if (err == hipSuccess) return ok();
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+constexpr int32_t kAutoPartitionTokens = 512;
+constexpr int32_t kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(pa_dtype dt) { return dt == PA_F16 ? 2 : 4; }
+
+size_t ws_align(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+pa_status check_dtype_shape(pa_dtype dtype, int32_t head_dim, int32_t block_size) {
+  if (dtype != PA_F32 && dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "dtype %d is not PA_F32 or PA_F16", (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 128)", head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not built (8, 16, 32)", block_size);
+  return PA_OK;
+}
+
+// Resolved partition length, or -1 with the last error set.
+int32_t resolve_partition(int32_t num_seqs, int32_t num_heads, int32_t block_size,
+                          int32_t max_context_len, int32_t partition_size) {
+  (void)num_seqs;
+  (void)num_heads;
+  if (block_size <= 0) {
+    fail(PA_ERR_INVALID_ARG, "block_size %d must be positive", block_size);
+    return -1;
+  }
+  if (max_context_len < 0) {
+    fail(PA_ERR_INVALID_ARG, "max_context_len %d is negative", max_context_len);
+    return -1;
+  }
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0)) {
+    fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a positive multiple of block_size %d",
+         partition_size, block_size);
+    return -1;
+  }
+  if (partition_size > 0) return partition_size;
+  return ((kAutoPartitionTokens + block_size - 1) / block_size) * block_size;
+}
+
+int32_t partitions_for(int32_t max_context_len, int32_t P) {
+  const int64_t np = (static_cast<int64_t>(max_context_len) + P - 1) / P;
+  return np < 1 ? 1 : static_cast<int32_t>(np);
+}
+
+size_t workspace_bytes_for(int32_t S, int32_t H, int32_t D, int32_t NP) {
+  if (NP <= 1) return 0;
+  const size_t states = static_cast<size_t>(S) * H * NP;
+  return 2 * ws_align(states * 4) + ws_align(states * D * 4);
+}
+
+struct DecodePlan {
+  pa::DecodeParams prm;
+  int32_t NP;
+};
+
+pa_status plan_decode(DecodePlan* plan, void* out, const void* query, const void* key_cache,
+                      const void* value_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                      pa_dtype dtype, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes) {
+  pa_status st = check_dtype_shape(dtype, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "sizes must be positive (num_seqs %d >= 0, num_heads %d, num_blocks %d, max_blocks_per_seq %d)",
+                num_seqs, num_heads, num_blocks, max_blocks_per_seq);
+  if (num_seqs > kMaxGridYZ || num_heads > kMaxGridYZ)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs %d and num_heads %d must be <= %d", num_seqs, num_heads,
+                kMaxGridYZ);
+  if (max_context_len < 0 ||
+      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARG, "max_context_len %d must be in [0, max_blocks_per_seq * block_size = %lld]",
+                max_context_len, static_cast<long long>(max_blocks_per_seq) * block_size);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  const int32_t P = resolve_partition(num_seqs, num_heads, block_size, max_context_len, partition_size);
+  if (P < 0) return PA_ERR_INVALID_ARG;
+  const int32_t NP = partitions_for(max_context_len, P);
+  plan->NP = NP;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL, "a required pointer is NULL (out, query, key_cache, value_cache, block_tables, context_lens)");
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_ERR_INVALID_ARG, "out, query and the caches must be 16-byte aligned");
+  const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, NP);
+  if (need > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+    if (workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  pa::DecodeParams& p = plan->prm;
+  p.out = out;
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  const size_t states = static_cast<size_t>(num_seqs) * num_heads * NP;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_m = need ? reinterpret_cast<float*>(ws) : nullptr;
+  p.ws_l = need ? reinterpret_cast<float*>(ws + ws_align(states * 4)) : nullptr;
+  p.ws_o = need ? reinterpret_cast<float*>(ws + 2 * ws_align(states * 4)) : nullptr;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.partition_tokens = P;
+  p.num_partitions = NP;
+  p.scale = scale;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t block_size,
+                                 int32_t max_context_len, int32_t partition_size) {
+  return resolve_partition(num_seqs, num_heads, block_size, max_context_len, partition_size);
+}
+
+int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_heads, int32_t block_size,
+                                 int32_t max_context_len, int32_t partition_size) {
+  const int32_t P = resolve_partition(num_seqs, num_heads, block_size, max_context_len, partition_size);
+  if (P < 0) return -1;
+  return partitions_for(max_context_len, P);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_context_len,
+                                 int32_t partition_size) {
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0) {
+    fail(PA_ERR_INVALID_ARG, "num_seqs %d, num_heads %d, head_dim %d out of range", num_seqs, num_heads,
+         head_dim);
+    return 0;
+  }
+  const int32_t P = resolve_partition(num_seqs, num_heads, block_size, max_context_len, partition_size);
+  if (P < 0) return 0;
+  return workspace_bytes_for(num_seqs, num_heads, head_dim, partitions_for(max_context_len, P));
+}
+
+pa_status pa_decode_partitions(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                               pa_dtype dtype, int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  DecodePlan plan;
+  pa_status st = plan_decode(&plan, out, query, key_cache, value_cache, block_tables, context_lens,
+                             num_seqs, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             max_context_len, scale, dtype, partition_size, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  return from_hip(pa::launch_decode_partitions(plan.prm, dtype == PA_F16, head_dim, block_size,
+                                               static_cast<hipStream_t>(stream)),
+                  "decode partition pass launch");
+}
+
+pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                           pa_dtype dtype, int32_t partition_size, void* stream) {
+  pa_status st = check_dtype_shape(dtype, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_heads <= 0 || num_seqs > kMaxGridYZ || num_heads > kMaxGridYZ)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs %d / num_heads %d out of range", num_seqs, num_heads);
+  const int32_t P = resolve_partition(num_seqs, num_heads, block_size, max_context_len, partition_size);
+  if (P < 0) return PA_ERR_INVALID_ARG;
+  const int32_t NP = partitions_for(max_context_len, P);
+  if (num_seqs == 0 || NP <= 1) return ok();  // nothing to merge
+  if (!out || !workspace || !context_lens)
+    return fail(PA_ERR_NULL, "out, workspace and context_lens must not be NULL");
+  const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, NP);
+  if (workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if (!aligned16(out) || !aligned16(workspace))
+    return fail(PA_ERR_INVALID_ARG, "out and workspace must be 16-byte aligned");
+  const size_t states = static_cast<size_t>(num_seqs) * num_heads * NP;
+  const char* ws = static_cast<const char*>(workspace);
+  pa::ReduceParams prm;
+  prm.out = out;
+  prm.ws_m = reinterpret_cast<const float*>(ws);
+  prm.ws_l = reinterpret_cast<const float*>(ws + ws_align(states * 4));
+  prm.ws_o = reinterpret_cast<const float*>(ws + 2 * ws_align(states * 4));
+  prm.context_lens = context_lens;
+  prm.num_seqs = num_seqs;
+  prm.num_heads = num_heads;
+  prm.partition_tokens = P;
+  prm.num_partitions = NP;
+  return from_hip(pa::launch_decode_reduce(prm, dtype == PA_F16, head_dim, static_cast<hipStream_t>(stream)),
+                  "decode reduce pass launch");
+}
+
+pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status st = pa_decode_partitions(out, query, key_cache, value_cache, block_tables, context_lens,
+                                      num_seqs, num_heads, head_dim, block_size, num_blocks,
+                                      max_blocks_per_seq, max_context_len, scale, dtype, partition_size,
+                                      workspace, workspace_bytes, stream);
+  if (st != PA_OK) return st;
+  return pa_decode_reduce(out, workspace, workspace_bytes, context_lens, num_seqs, num_heads, head_dim,
+                          block_size, max_context_len, dtype, partition_size, stream);
+}
+
+pa_status pa_cache_append(void* key_cache, void* value_cache, const void* key, const void* value,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                          void* stream) {
+  pa_status st = check_dtype_shape(dtype, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0 || num_heads <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_tokens %d >= 0, num_heads %d > 0, num_blocks %d > 0 required",
+                num_tokens, num_heads, num_blocks);
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size exceeds the int32 slot range");
+  const int32_t row_bytes = head_dim * static_cast<int32_t>(elem_bytes(dtype));
+  const int64_t threads = static_cast<int64_t>(num_tokens) * num_heads * (row_bytes / 16);
+  if ((threads + 255) / 256 > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_tokens * num_heads too large for one launch");
+  if (num_tokens == 0) return ok();
+  if (!key_cache || !value_cache || !key || !value || !slot_mapping)
+    return fail(PA_ERR_NULL, "a required pointer is NULL (key_cache, value_cache, key, value, slot_mapping)");
+  if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned16(key) || !aligned16(value))
+    return fail(PA_ERR_INVALID_ARG, "caches and key/value rows must be 16-byte aligned");
+  pa::AppendParams prm;
+  prm.key_cache = key_cache;
+  prm.value_cache = value_cache;
+  prm.key = key;
+  prm.value = value;
+  prm.slot_mapping = slot_mapping;
+  prm.num_tokens = num_tokens;
+  prm.num_heads = num_heads;
+  prm.block_size = block_size;
+  prm.row_bytes = row_bytes;
+  return from_hip(pa::launch_cache_append(prm, static_cast<hipStream_t>(stream)), "cache append launch");
+}
+
+pa_status pa_block_copy(void* key_cache, void* value_cache, const int32_t* block_pairs, int32_t num_pairs,
+                        int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                        pa_dtype dtype, void* stream) {
+  pa_status st = check_dtype_shape(dtype, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0 || num_heads <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_pairs %d >= 0, num_heads %d > 0, num_blocks %d > 0 required",
+                num_pairs, num_heads, num_blocks);
+  if (num_pairs == 0) return ok();
+  if (!key_cache || !value_cache || !block_pairs)
+    return fail(PA_ERR_NULL, "a required pointer is NULL (key_cache, value_cache, block_pairs)");
+  if (!aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_ERR_INVALID_ARG, "caches must be 16-byte aligned");
+  pa::CopyParams prm;
+  prm.key_cache = key_cache;
+  prm.value_cache = value_cache;
+  prm.block_pairs = block_pairs;
+  prm.num_pairs = num_pairs;
+  prm.block_bytes = static_cast<int64_t>(num_heads) * block_size * head_dim * static_cast<int64_t>(elem_bytes(dtype));
+  return from_hip(pa::launch_block_copy(prm, static_cast<hipStream_t>(stream)), "block copy launch");
+}
+
+}  // extern "C"

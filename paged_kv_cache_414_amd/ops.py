@@ -1,0 +1,230 @@
+"""Python binding of ``libpa.so``: the C-ABI entry points under the same names.
+
+Argument marshalling only: shapes are read from the tensors, pointers and the
+current HIP stream are passed through, and a non-OK status raises
+:class:`PagedAttentionError` with the library's message.  Every step of the path
+runs in the HIP kernels; there is no fallback.  Importing this module loads the
+library and raises if it has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+import torch
+
+LIB_PATH = pathlib.Path(__file__).resolve().with_name("libpa.so")
+
+PA_F32 = 0
+PA_F16 = 1
+_DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16}
+_STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_INVALID_ARG", 3: "PA_ERR_UNSUPPORTED",
+           4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP"}
+
+# name -> (restype, argtypes), mirroring include/pa.h
+_i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+SIGNATURES = {
+    "pa_abi_version": (_i32, []),
+    "pa_status_string": (ctypes.c_char_p, [_i32]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_num_partitions": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                         _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_reduce": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _vp]),
+    "pa_cache_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _vp]),
+    "pa_block_copy": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+}
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library(path: pathlib.Path | str = LIB_PATH) -> ctypes.CDLL:
+    path = pathlib.Path(path)
+    if not path.exists():
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m paged_kv_cache_414_amd.build`")
+    lib = ctypes.CDLL(str(path))
+    for name, (restype, argtypes) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = restype
+        fn.argtypes = argtypes
+    return lib
+
+
+lib = load_library()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PagedAttentionError(status, lib.pa_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpa must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream, device) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype} (float32 or float16)") from None
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1 or next(iter(devs)).type != "cuda":
+        raise ValueError(f"all tensors must be on one GPU, got {devs}")
+    return next(iter(devs))
+
+
+def _int32(*ts):
+    for t in ts:
+        if t.dtype != torch.int32:
+            raise ValueError("index tensors must be int32")
+
+
+# ----------------------------------------------------------------------------------
+# planning
+# ----------------------------------------------------------------------------------
+
+def pa_decode_partition_size(num_seqs, num_heads, block_size, max_context_len,
+                             partition_size=0) -> int:
+    p = lib.pa_decode_partition_size(num_seqs, num_heads, block_size, max_context_len,
+                                     partition_size)
+    if p < 0:
+        raise PagedAttentionError(2, lib.pa_last_error().decode())
+    return p
+
+
+def pa_decode_num_partitions(num_seqs, num_heads, block_size, max_context_len,
+                             partition_size=0) -> int:
+    n = lib.pa_decode_num_partitions(num_seqs, num_heads, block_size, max_context_len,
+                                     partition_size)
+    if n < 0:
+        raise PagedAttentionError(2, lib.pa_last_error().decode())
+    return n
+
+
+def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, block_size, max_context_len,
+                              partition_size=0) -> int:
+    return int(lib.pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, block_size,
+                                             max_context_len, partition_size))
+
+
+def workspace_for(query: torch.Tensor, key_cache: torch.Tensor, max_context_len: int,
+                  partition_size: int = 0) -> torch.Tensor | None:
+    """Device buffer of the size pa_decode needs (None when none is needed)."""
+    s, h, d = query.shape
+    n = pa_decode_workspace_bytes(s, h, d, key_cache.shape[2], max_context_len,
+                                  partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=query.device)
+
+
+# ----------------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------------
+
+def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                 max_context_len, partition_size, workspace, stream):
+    dev = _same_device(out, query, key_cache, value_cache, block_tables, context_lens)
+    _int32(block_tables, context_lens)
+    if not (out.dtype == query.dtype == key_cache.dtype == value_cache.dtype):
+        raise ValueError("out, query and the caches must share one dtype")
+    s, h, d = query.shape
+    nb, hk, bs, dk = key_cache.shape
+    if (hk, dk) != (h, d) or value_cache.shape != key_cache.shape or out.shape != query.shape:
+        raise ValueError("shape mismatch between query/out [S,H,D] and caches [NB,H,bs,D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.shape != (s,):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+            _ptr(context_lens), s, h, d, bs, nb, block_tables.shape[1], int(max_context_len),
+            float(scale), _dtype(query), int(partition_size), _ptr(workspace), ws_bytes,
+            _stream(stream, dev))
+
+
+def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+              max_context_len, partition_size=0, workspace=None, stream=None):
+    """Paged decode attention into ``out`` [S, H, D] (see include/pa.h)."""
+    _check(lib.pa_decode(*_decode_args(out, query, key_cache, value_cache, block_tables,
+                                       context_lens, scale, max_context_len,
+                                       partition_size, workspace, stream)))
+    return out
+
+
+def pa_decode_partitions(out, query, key_cache, value_cache, block_tables, context_lens,
+                         scale, max_context_len, partition_size=0, workspace=None,
+                         stream=None):
+    """First (partition) pass of pa_decode alone."""
+    _check(lib.pa_decode_partitions(*_decode_args(out, query, key_cache, value_cache,
+                                                  block_tables, context_lens, scale,
+                                                  max_context_len, partition_size,
+                                                  workspace, stream)))
+    return out
+
+
+def pa_decode_reduce(out, workspace, context_lens, block_size, max_context_len,
+                     partition_size=0, stream=None):
+    """Second (merge) pass of pa_decode alone."""
+    dev = _same_device(out, context_lens)
+    _int32(context_lens)
+    s, h, d = out.shape
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode_reduce(_ptr(out), _ptr(workspace), ws_bytes, _ptr(context_lens), s,
+                                h, d, int(block_size), int(max_context_len), _dtype(out),
+                                int(partition_size), _stream(stream, dev)))
+    return out
+
+
+def pa_cache_append(key_cache, value_cache, key, value, slot_mapping, stream=None):
+    """Write key/value rows [T, H, D] into the caches at ``slot_mapping`` [T]."""
+    dev = _same_device(key_cache, value_cache, key, value, slot_mapping)
+    _int32(slot_mapping)
+    if not (key_cache.dtype == value_cache.dtype == key.dtype == value.dtype):
+        raise ValueError("caches and key/value must share one dtype")
+    nb, h, bs, d = key_cache.shape
+    t = key.shape[0]
+    if key.shape != (t, h, d) or value.shape != key.shape or slot_mapping.shape != (t,):
+        raise ValueError("key/value must be [T, H, D] and slot_mapping [T]")
+    if value_cache.shape != key_cache.shape:
+        raise ValueError("key and value caches differ in shape")
+    _check(lib.pa_cache_append(_ptr(key_cache), _ptr(value_cache), _ptr(key), _ptr(value),
+                               _ptr(slot_mapping), t, h, d, bs, nb, _dtype(key),
+                               _stream(stream, dev)))
+
+
+def pa_block_copy(key_cache, value_cache, block_pairs, stream=None):
+    """Copy whole blocks: for each row (src, dst) of ``block_pairs`` [n, 2]."""
+    dev = _same_device(key_cache, value_cache, block_pairs)
+    _int32(block_pairs)
+    nb, h, bs, d = key_cache.shape
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2]")
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("key and value caches differ")
+    _check(lib.pa_block_copy(_ptr(key_cache), _ptr(value_cache), _ptr(block_pairs),
+                             block_pairs.shape[0], h, d, bs, nb, _dtype(key_cache),
+                             _stream(stream, dev)))

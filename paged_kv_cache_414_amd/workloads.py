@@ -26,16 +26,18 @@ valid index, never an out-of-range one).
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 
 F16_NAN_BITS = np.uint16(0x7E00)
 F32_NAN_BITS = np.uint32(0x7FC00000)
 
-# Chunk of the pool filled per numpy call, in elements (bounds temporary memory).
-_FILL_CHUNK = 1 << 25
+# Elements per independently drawn chunk of a large array (bounds temporary memory).
+_FILL_CHUNK = 1 << 22
 
 
 @dataclasses.dataclass
@@ -70,12 +72,28 @@ class DecodeBatch:
 # ----------------------------------------------------------------------------------
 
 def fill_normal(rng: np.random.Generator, out: np.ndarray) -> None:
-    """Fill ``out`` (float16 or float32, C-contiguous) with N(0,1) drawn in float32."""
+    """Fill ``out`` (float16 or float32, C-contiguous) with N(0,1) drawn in float32.
+
+    Small arrays are drawn from ``rng`` directly.  Large ones are cut into fixed
+    chunks of _FILL_CHUNK elements, chunk i drawn from the i-th child generator
+    spawned from ``rng``, on a few threads; the values do not depend on the number
+    of threads."""
     flat = out.reshape(-1)
-    for start in range(0, flat.size, _FILL_CHUNK):
+    if flat.size <= _FILL_CHUNK:
+        flat[:] = rng.standard_normal(flat.size, dtype=np.float32)
+        return
+    starts = list(range(0, flat.size, _FILL_CHUNK))
+    children = rng.spawn(len(starts))
+
+    def fill(i):
+        start = starts[i]
         stop = min(flat.size, start + _FILL_CHUNK)
-        vals = rng.standard_normal(stop - start, dtype=np.float32)
+        vals = children[i].standard_normal(stop - start, dtype=np.float32)
         flat[start:stop] = vals  # float16 destination: numpy rounds to nearest even
+
+    workers = max(1, min(16, os.cpu_count() or 1, len(starts)))
+    with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+        list(pool.map(fill, range(len(starts))))
 
 
 def normal(rng: np.random.Generator, shape, dtype) -> np.ndarray:

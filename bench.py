@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition, 0 = auto")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one pa_block_copy of a known size (counter calibration)")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -65,8 +67,8 @@ def time_launches(fn, n, torch):
 
 
 def cpu_baseline(batch, budget_s):
-    """The oracle as it stands, single-threaded BLAS, over (seq, head) pairs in order
-    until the time budget is spent."""
+    """The oracle as it stands, single-threaded BLAS, over the batch's (seq, head)
+    pairs in order, repeating the batch until the time budget is spent."""
     import oracle
     from threadpoolctl import threadpool_limits
 
@@ -77,17 +79,19 @@ def cpu_baseline(batch, budget_s):
     pairs = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        for s in range(batch.num_seqs):
-            for h in range(h_count):
-                oracle.decode_one(batch.q[s, h], batch.k_pool, batch.v_pool,
-                                  batch.block_tables[s], batch.context_lens[s], h, batch.scale)
-                done_tokens += int(batch.context_lens[s])
-                pairs += 1
-                if time.perf_counter() - t0 >= budget_s:
-                    break
-            else:
-                continue
-            break
+        while time.perf_counter() - t0 < budget_s:
+            for s in range(batch.num_seqs):
+                for h in range(h_count):
+                    oracle.decode_one(batch.q[s, h], batch.k_pool, batch.v_pool,
+                                      batch.block_tables[s], batch.context_lens[s], h,
+                                      batch.scale)
+                    done_tokens += int(batch.context_lens[s])
+                    pairs += 1
+                    if time.perf_counter() - t0 >= budget_s:
+                        break
+                else:
+                    continue
+                break
         elapsed = time.perf_counter() - t0
     nbytes = metrics.kv_bytes_per_token(1, 1, batch.head_dim, batch.q.itemsize) * done_tokens
     return {
@@ -95,10 +99,26 @@ def cpu_baseline(batch, budget_s):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"first {pairs} (seq, head) pairs of the batch in order "
+        "sample": (f"{pairs} (seq, head) pairs of the batch in order, repeating the batch "
                    f"({done_tokens} tokens, {elapsed:.1f} s), fp64 numpy, BLAS limited to 1 thread"),
         "seq_steps_per_s": round(pairs / h_count / elapsed, 4),
     }
+
+
+def copy_probe(torch, ops, metrics, pairs=1024):
+    """One pa_block_copy of ``pairs`` blocks of 32 heads x 16 x 128 fp16 (128 KiB per
+    block for K and for V): a plain copy of known size, run once, whose memory
+    counters calibrate those of the decode kernel."""
+    block = (32, 16, 128)
+    kc = torch.zeros((2 * pairs, *block), dtype=torch.float16, device="cuda")
+    vc = torch.zeros_like(kc)
+    pairs_d = torch.stack([torch.arange(pairs), torch.arange(pairs, 2 * pairs)], dim=1)
+    pairs_d = pairs_d.to(torch.int32).cuda()
+    torch.cuda.synchronize()
+    ops.pa_block_copy(kc, vc, pairs_d)
+    torch.cuda.synchronize()
+    moved = metrics.block_copy_bytes(pairs, *block[:2], block[2], 2) // 2
+    return {"kernel": "block_copy_kernel", "read_bytes": moved, "write_bytes": moved}
 
 
 def main():
@@ -204,6 +224,8 @@ def main():
             "algorithmic_bytes_per_launch": kv,
         },
     }
+    if args.copy_probe:
+        record["copy_probe"] = copy_probe(torch, ops, metrics)
     if args.cpu_seconds > 0:
         log(args, f"CPU oracle baseline ({args.cpu_seconds:.0f} s budget)")
         record["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)

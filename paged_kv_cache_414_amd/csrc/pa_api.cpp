@@ -36,7 +36,15 @@ pa_status from_hip(hipError_t err, const char* what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
-constexpr int32_t kAutoPartitionTokens = 512;
+// Library choice of the partition length: start from the whole longest context
+// (one partition per sequence, no merge pass) and halve while the launch would hold
+// fewer than kAutoMinUnits (sequence, head, partition) work units, i.e. about twelve
+// workgroups per compute unit of a 256-CU MI355X, never going below
+// kAutoMinPartitionTokens.  Measured on MI355X: long partitions stream at a higher
+// rate (less per-workgroup set-up and fewer short tail partitions) as long as the
+// grid keeps every CU busy.
+constexpr int64_t kAutoMinUnits = 3072;
+constexpr int32_t kAutoMinPartitionTokens = 256;
 constexpr int32_t kMaxGridYZ = 65535;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -54,11 +62,11 @@ pa_status check_dtype_shape(pa_dtype dtype, int32_t head_dim, int32_t block_size
   return PA_OK;
 }
 
+int32_t round_up(int64_t x, int32_t m) { return static_cast<int32_t>(((x + m - 1) / m) * m); }
+
 // Resolved partition length, or -1 with the last error set.
 int32_t resolve_partition(int32_t num_seqs, int32_t num_heads, int32_t block_size,
                           int32_t max_context_len, int32_t partition_size) {
-  (void)num_seqs;
-  (void)num_heads;
   if (block_size <= 0) {
     fail(PA_ERR_INVALID_ARG, "block_size %d must be positive", block_size);
     return -1;
@@ -73,7 +81,16 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_heads, int32_t block_siz
     return -1;
   }
   if (partition_size > 0) return partition_size;
-  return ((kAutoPartitionTokens + block_size - 1) / block_size) * block_size;
+  const int64_t pairs = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_heads > 0 ? num_heads : 1);
+  const int32_t floor_p = round_up(kAutoMinPartitionTokens, block_size);
+  int32_t P = round_up(max_context_len > 0 ? max_context_len : 1, block_size);
+  while (P > floor_p) {
+    const int64_t units = pairs * ((static_cast<int64_t>(max_context_len) + P - 1) / P);
+    if (units >= kAutoMinUnits) break;
+    const int32_t half = round_up(P / 2, block_size);
+    P = half > floor_p ? half : floor_p;
+  }
+  return P;
 }
 
 int32_t partitions_for(int32_t max_context_len, int32_t P) {

@@ -35,8 +35,19 @@ namespace pa {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// Build-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 8  // wave64s per decode workgroup
+#endif
+#ifndef PA_KV_LOADS_IN_FLIGHT
+#define PA_KV_LOADS_IN_FLIGHT 8  // 16-byte K+V loads per lane issued before their use
+#endif
+#ifndef PA_NONTEMPORAL_KV
+#define PA_NONTEMPORAL_KV 1  // 1: K/V loads carry the non-temporal (streaming) hint
+#endif
+
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
+constexpr int kWaves = PA_DECODE_WAVES;
 constexpr int kThreads = kWave * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -46,6 +57,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+// K/V rows are read exactly once per call.
+__device__ __forceinline__ u32x4 load_kv16(const void* p) {
+#if PA_NONTEMPORAL_KV
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
 }
 
 __device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -127,8 +147,9 @@ struct Geometry {
   static constexpr int kLanesPerTok = D / kVec;            // lanes covering one token row
   static constexpr int kTokPerLoad = kWave / kLanesPerTok; // token rows per wave-wide load
   static constexpr int kLoads = BS / kTokPerLoad;          // loads per (block, head) chunk
-  // blocks fetched together per wave: about 16 x 16 B of K+V in flight per lane
-  static constexpr int kUnroll = kLoads >= 8 ? 1 : 8 / kLoads;
+  // blocks fetched together per wave: PA_KV_LOADS_IN_FLIGHT 16-byte loads per lane
+  static constexpr int kUnroll =
+      2 * kLoads >= PA_KV_LOADS_IN_FLIGHT ? 1 : PA_KV_LOADS_IN_FLIGHT / (2 * kLoads);
   static_assert(D % kVec == 0 && kWave % kLanesPerTok == 0, "head_dim");
   static_assert(BS % kTokPerLoad == 0, "block_size");
 };
@@ -271,14 +292,14 @@ __global__ __launch_bounds__(kThreads) void decode_partitions_kernel(DecodeParam
         const int phys = __builtin_amdgcn_readlane(ids, j + u);
         const T* kp = k_head + static_cast<size_t>(phys) * block_stride + lane_off;
 #pragma unroll
-        for (int i = 0; i < G::kLoads; ++i) kr[u][i] = load16(kp + i * G::kTokPerLoad * D);
+        for (int i = 0; i < G::kLoads; ++i) kr[u][i] = load_kv16(kp + i * G::kTokPerLoad * D);
       }
 #pragma unroll
       for (int u = 0; u < G::kUnroll; ++u) {
         const int phys = __builtin_amdgcn_readlane(ids, j + u);
         const T* vp = v_head + static_cast<size_t>(phys) * block_stride + lane_off;
 #pragma unroll
-        for (int i = 0; i < G::kLoads; ++i) vr[u][i] = load16(vp + i * G::kTokPerLoad * D);
+        for (int i = 0; i < G::kLoads; ++i) vr[u][i] = load_kv16(vp + i * G::kTokPerLoad * D);
       }
 #pragma unroll
       for (int u = 0; u < G::kUnroll; ++u)
@@ -292,9 +313,9 @@ __global__ __launch_bounds__(kThreads) void decode_partitions_kernel(DecodeParam
       const T* kp = k_head + static_cast<size_t>(phys) * block_stride + lane_off;
       const T* vp = v_head + static_cast<size_t>(phys) * block_stride + lane_off;
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) kr[i] = load16(kp + i * G::kTokPerLoad * D);
+      for (int i = 0; i < G::kLoads; ++i) kr[i] = load_kv16(kp + i * G::kTokPerLoad * D);
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) vr[i] = load16(vp + i * G::kTokPerLoad * D);
+      for (int i = 0; i < G::kLoads; ++i) vr[i] = load_kv16(vp + i * G::kTokPerLoad * D);
       fold_block<T, D, BS, false>(st, q, kr, vr, scale_log2, row, BS);
     }
     // the partly filled last block of the partition, if this chunk holds it
@@ -306,9 +327,9 @@ __global__ __launch_bounds__(kThreads) void decode_partitions_kernel(DecodeParam
       const T* kp = k_head + static_cast<size_t>(phys) * block_stride + lane_off;
       const T* vp = v_head + static_cast<size_t>(phys) * block_stride + lane_off;
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) kr[i] = load16(kp + i * G::kTokPerLoad * D);
+      for (int i = 0; i < G::kLoads; ++i) kr[i] = load_kv16(kp + i * G::kTokPerLoad * D);
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) vr[i] = load16(vp + i * G::kTokPerLoad * D);
+      for (int i = 0; i < G::kLoads; ++i) vr[i] = load_kv16(vp + i * G::kTokPerLoad * D);
       fold_block<T, D, BS, true>(st, q, kr, vr, scale_log2, row, tok_end - blk * BS);
     }
   }

@@ -29,6 +29,33 @@ import numpy as np
 
 METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 
+# HBM bytes per launch of the partition pass on this workload (seed 2), from two
+# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
+# known-size block copy (FETCH_SIZE x 1.9963, WRITE_SIZE x 1.000); the commands and
+# raw values are in profiles/decode_partitions_llama7b_pmc.md.  Valid only for the
+# kernel source they were taken on.
+MEASURED_TRAFFIC = {
+    "kernel_source_sha256": "84d0f19d381bd32c881f30d65736f473380c86306f3ac07e538bcafe32f7a7ad",
+    "seed": 2,
+    "partition_tokens": 2048,
+    "read_bytes": 1934578720,
+    "write_bytes": 786432,
+}
+KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                             "paged_kv_cache_414_amd", "csrc", "pa_kernels.hip")
+
+
+def measured_traffic(seed, partition_tokens):
+    """Counter-measured HBM bytes per launch, or None if the kernel source or the
+    workload differ from the ones the counters were taken on."""
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    t = MEASURED_TRAFFIC
+    if sha != t["kernel_source_sha256"] or seed != t["seed"] or partition_tokens != t["partition_tokens"]:
+        return None
+    return t["read_bytes"] + t["write_bytes"]
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__,
@@ -40,6 +67,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition, 0 = auto")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--no-mixes", dest="mixes", action="store_false",
+                    help="skip the continuous-batching and shared-prefix step mixes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one pa_block_copy of a known size (counter calibration)")
     ap.add_argument("--quiet", action="store_true")
@@ -102,6 +131,36 @@ def cpu_baseline(batch, budget_s):
         "sample": (f"{pairs} (seq, head) pairs of the batch in order, repeating the batch "
                    f"({done_tokens} tokens, {elapsed:.1f} s), fp64 numpy, BLAS limited to 1 thread"),
         "seq_steps_per_s": round(pairs / h_count / elapsed, 4),
+    }
+
+
+def run_mix(cls_name, seed, torch, args):
+    """One full run of a step mix: wall-clock seq-steps/s (host block manager, the
+    small per-step H2D copies and the launches included; synthetic inputs staged in
+    HBM beforehand) and the last step's decode re-timed alone."""
+    from paged_kv_cache_414_amd import metrics, steps
+
+    log(args, f"step mix {cls_name}")
+    mix = getattr(steps, cls_name)(seed=seed)
+    mix.prepare()  # every step's synthetic inputs drawn and placed in HBM
+    t0 = time.perf_counter()
+    rows = 0
+    for k in range(mix.steps):
+        ctx = mix.run_step(k)
+        rows += len(ctx)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = time_launches(mix.decode_again, 50, torch)
+    kv = mix.kv_bytes(ctx)
+    return {
+        "steps": mix.steps,
+        "seq_steps_per_s_wall": round(rows / wall, 1),
+        "wall_s": round(wall, 4),
+        "copy_on_write_pairs": mix.copies_total,
+        "last_step_decode_ms": round(ms, 5),
+        "last_step_decode_kv_gbps": round(metrics.gbps(kv, ms * 1e-3), 1),
+        "last_step_sum_context": int(ctx.sum()),
+        "note": "decode GB/s at this size may include Infinity Cache hits (working set < 256 MB)",
     }
 
 
@@ -219,11 +278,15 @@ def main():
             "peak": metrics.HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / metrics.HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.seed, part),
             "avg_launch_ms": round(ms_part, 5),
             "algorithmic_bytes_per_launch": kv,
         },
     }
+    if args.mixes:
+        record["step_mixes"] = {name: run_mix(cls, seed, torch, args)
+                                for name, cls, seed in (("continuous_batching", "ContinuousBatching", 3),
+                                                        ("shared_prefix_cow", "SharedPrefix", 4))}
     if args.copy_probe:
         record["copy_probe"] = copy_probe(torch, ops, metrics)
     if args.cpu_seconds > 0:

@@ -206,8 +206,9 @@ def brute_force_decode(q, k_pool, v_pool, block_tables, context_lens, scale):
 # writes into the pool
 # ----------------------------------------------------------------------------------
 
-def cache_append(k_pool, v_pool, key, value, slot_mapping):
-    """Return copies of the pools with row i of key/value written at slot_mapping[i].
+def cache_append(k_pool, v_pool, key, value, slot_mapping, inplace=False):
+    """Pools with row i of key/value written at slot_mapping[i]: copies, or the given
+    arrays themselves when ``inplace``.
 
     key/value [T, H, D]; a negative slot leaves the pools untouched for that row.
     Slots must be distinct."""
@@ -215,8 +216,8 @@ def cache_append(k_pool, v_pool, key, value, slot_mapping):
     live = [int(s) for s in slot_mapping if int(s) >= 0]
     if len(set(live)) != len(live):
         raise ValueError("slot_mapping repeats a slot")
-    k_out = k_pool.copy()
-    v_out = v_pool.copy()
+    k_out = k_pool if inplace else k_pool.copy()
+    v_out = v_pool if inplace else v_pool.copy()
     for i, slot in enumerate(slot_mapping):
         slot = int(slot)
         if slot < 0:
@@ -227,8 +228,9 @@ def cache_append(k_pool, v_pool, key, value, slot_mapping):
     return k_out, v_out
 
 
-def block_copy(k_pool, v_pool, pairs):
-    """Return copies of the pools with block dst := block src for each (src, dst).
+def block_copy(k_pool, v_pool, pairs, inplace=False):
+    """Pools with block dst := block src for each (src, dst): copies, or the given
+    arrays themselves when ``inplace``.
 
     All sources are read before any destination is written.  Destinations must be
     distinct and must not be sources."""
@@ -241,8 +243,8 @@ def block_copy(k_pool, v_pool, pairs):
         raise ValueError("block_copy destination is also a source")
     k_src = [k_pool[a].copy() for a, _ in pairs]
     v_src = [v_pool[a].copy() for a, _ in pairs]
-    k_out = k_pool.copy()
-    v_out = v_pool.copy()
+    k_out = k_pool if inplace else k_pool.copy()
+    v_out = v_pool if inplace else v_pool.copy()
     for (_, b), kb, vb in zip(pairs, k_src, v_src):
         k_out[b] = kb
         v_out[b] = vb

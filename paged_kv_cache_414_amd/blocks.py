@@ -116,7 +116,10 @@ class BlockManager:
             raise OutOfBlocks(f"{n_blk} blocks needed, {self.alloc.num_free} free")
         seq = Sequence(seq_id, [self.alloc.allocate() for _ in range(n_blk)], int(num_tokens))
         self.seqs[seq_id] = seq
-        return np.array([self.slot(seq_id, p) for p in range(num_tokens)], dtype=np.int32)
+        # token p sits in block p // bs at offset p % bs
+        per_block = np.asarray(seq.blocks, dtype=np.int64)[:, None] * self.block_size
+        slots = (per_block + np.arange(self.block_size)[None, :]).reshape(-1)
+        return slots[:num_tokens].astype(np.int32)
 
     def fork(self, parent_id: int, child_id: int) -> None:
         """The child shares every block of the parent (reference counts + 1)."""

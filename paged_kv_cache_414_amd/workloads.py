@@ -74,15 +74,14 @@ class DecodeBatch:
 def fill_normal(rng: np.random.Generator, out: np.ndarray) -> None:
     """Fill ``out`` (float16 or float32, C-contiguous) with N(0,1) drawn in float32.
 
-    Small arrays are drawn from ``rng`` directly.  Large ones are cut into fixed
-    chunks of _FILL_CHUNK elements, chunk i drawn from the i-th child generator
-    spawned from ``rng``, on a few threads; the values do not depend on the number
-    of threads."""
+    The array is cut into fixed chunks of _FILL_CHUNK elements; chunk i is drawn from
+    the i-th child generator spawned from ``rng``, on a few threads for large arrays.
+    The values depend neither on the number of threads nor, for a given leading
+    part of the array, on the array's total size."""
     flat = out.reshape(-1)
-    if flat.size <= _FILL_CHUNK:
-        flat[:] = rng.standard_normal(flat.size, dtype=np.float32)
-        return
     starts = list(range(0, flat.size, _FILL_CHUNK))
+    if not starts:
+        return
     children = rng.spawn(len(starts))
 
     def fill(i):
@@ -92,6 +91,9 @@ def fill_normal(rng: np.random.Generator, out: np.ndarray) -> None:
         flat[start:stop] = vals  # float16 destination: numpy rounds to nearest even
 
     workers = max(1, min(16, os.cpu_count() or 1, len(starts)))
+    if workers == 1:
+        fill(0)
+        return
     with concurrent.futures.ThreadPoolExecutor(workers) as pool:
         list(pool.map(fill, range(len(starts))))
 
@@ -265,11 +267,14 @@ class StepDraws:
         s = self.spec
         return normal(self.rng(step, 2), (n, s.num_heads, s.head_dim), s.dtype)
 
-    def prompt_kv(self, step: int, index: int, n_tokens: int) -> tuple[np.ndarray, np.ndarray]:
+    def prompt_kv(self, step: int, lens) -> tuple[np.ndarray, np.ndarray]:
+        """K and V rows of the prompts admitted at ``step`` (step -1: before the first
+        step), concatenated in admission order: [sum(lens), H, D] each."""
         s = self.spec
-        rng = self.rng(step, 1000 + int(index))
-        k = normal(rng, (n_tokens, s.num_heads, s.head_dim), s.dtype)
-        v = normal(rng, (n_tokens, s.num_heads, s.head_dim), s.dtype)
+        rng = self.rng(step, 4)
+        n = int(np.sum(lens))
+        k = normal(rng, (n, s.num_heads, s.head_dim), s.dtype)
+        v = normal(rng, (n, s.num_heads, s.head_dim), s.dtype)
         return k, v
 
 
@@ -296,7 +301,7 @@ class ContinuousBatchingDraws(StepDraws):
                                   replace=False)).astype(np.int32)
 
     def replacement_prompt_lens(self, step: int) -> np.ndarray:
-        rng = self.rng(step, 4)
+        rng = self.rng(step, 6)
         return rng.integers(self.prompt_low, self.prompt_high + 1,
                             size=self.finish_count).astype(np.int32)
 

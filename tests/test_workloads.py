@@ -62,11 +62,19 @@ def test_padding_entries_point_at_dead_blocks():
 
 
 def test_half_precision_rounding_is_nearest_even():
-    rng = np.random.default_rng(0)
+    """A small fill is the first spawned child's float32 draws rounded to fp16."""
     out = np.empty(1000, dtype=np.float16)
     workloads.fill_normal(np.random.default_rng(0), out)
-    ref = rng.standard_normal(1000, dtype=np.float32).astype(np.float16)
-    assert np.array_equal(out.view(np.uint16), ref.view(np.uint16))
+    ref = np.random.default_rng(0).spawn(1)[0].standard_normal(1000, dtype=np.float32)
+    assert np.array_equal(out.view(np.uint16), ref.astype(np.float16).view(np.uint16))
+
+
+def test_fill_prefix_does_not_depend_on_total_size():
+    a = np.empty(3 * workloads._FILL_CHUNK + 5, dtype=np.float16)
+    b = np.empty(workloads._FILL_CHUNK + 7, dtype=np.float16)
+    workloads.fill_normal(np.random.default_rng(9), a)
+    workloads.fill_normal(np.random.default_rng(9), b)
+    assert np.array_equal(a[:b.size].view(np.uint16), b.view(np.uint16))
 
 
 def test_small_llama_shaped_batch():

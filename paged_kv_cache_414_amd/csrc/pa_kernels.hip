@@ -45,6 +45,14 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #ifndef PA_NONTEMPORAL_KV
 #define PA_NONTEMPORAL_KV 1  // 1: K/V loads carry the non-temporal (streaming) hint
 #endif
+#ifndef PA_WAVES_PER_EU
+#define PA_WAVES_PER_EU 0  // >0: cap registers so this many waves fit per SIMD
+#endif
+#if PA_WAVES_PER_EU > 0
+#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
+#else
+#define PA_OCCUPANCY
+#endif
 
 constexpr int kWave = 64;
 constexpr int kWaves = PA_DECODE_WAVES;
@@ -77,11 +85,18 @@ constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 
+// Every row and bank enabled with bound_ctrl set, so the compiler folds the move
+// into the add that consumes it (one v_add_f32 with a DPP source operand).
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
 }
+
+// 2^x with the hardware transcendental unit (v_exp_f32).  Softmax weights below
+// 2^-126 of the running maximum may flush to zero, which changes no sum by more
+// than that amount.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Sum over groups of kLanes consecutive lanes; every lane of a group receives the
 // same bits (each stage adds two equal-valued operands in either order).
@@ -185,9 +200,9 @@ __device__ __forceinline__ void fold_block(RowState<Geometry<T, D, BS>::kVec>& s
   const float m_new = fmaxf(st.m, top);
   float alpha;
   if constexpr (kTail) {
-    alpha = (m_new == -INFINITY) ? 1.0f : exp2f(st.m - m_new);
+    alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(st.m - m_new);
   } else {
-    alpha = exp2f(st.m - m_new);  // m_new is finite: every token of the block is live
+    alpha = fast_exp2(st.m - m_new);  // m_new is finite: every token of the block is live
   }
   st.l *= alpha;
 #pragma unroll
@@ -197,7 +212,7 @@ __device__ __forceinline__ void fold_block(RowState<Geometry<T, D, BS>::kVec>& s
     if constexpr (kTail) {
       if (i * G::kTokPerLoad + row >= n_valid) continue;
     }
-    const float p = exp2f(z[i] - m_new);
+    const float p = fast_exp2(z[i] - m_new);
     st.l += p;
     Lane16<T>::axpy(p, vr[i], st.acc);
   }
@@ -209,78 +224,30 @@ template <int kVec>
 __device__ __forceinline__ void merge_state(RowState<kVec>& a, float m_b, float l_b,
                                             const float* acc_b) {
   const float m = fmaxf(a.m, m_b);
-  const float fa = (a.m == -INFINITY) ? 0.0f : exp2f(a.m - m);
-  const float fb = (m_b == -INFINITY) ? 0.0f : exp2f(m_b - m);
+  const float fa = (a.m == -INFINITY) ? 0.0f : fast_exp2(a.m - m);
+  const float fb = (m_b == -INFINITY) ? 0.0f : fast_exp2(m_b - m);
   a.l = a.l * fa + l_b * fb;
 #pragma unroll
   for (int j = 0; j < kVec; ++j) a.acc[j] = a.acc[j] * fa + acc_b[j] * fb;
   a.m = m;
 }
 
-// ---------------------------------------------------------------------------------
-// decode, partition pass
-// grid (max partitions, heads, seqs), kThreads threads
-// ---------------------------------------------------------------------------------
-
+// Fold this wave's blocks of one (partition, head) into its row state.  Lane j of
+// `ids` holds the physical id of the wave's j-th block (the first kWave of them);
+// a longer list is fetched kWave at a time from `my_table` (stride kWaves).
 template <typename T, int D, int BS>
-__global__ __launch_bounds__(kThreads) void decode_partitions_kernel(DecodeParams prm) {
+__device__ __forceinline__ void attend_blocks(RowState<Geometry<T, D, BS>::kVec>& st,
+                                              const u32x4& q, int ids, const int* my_table,
+                                              const T* k_head, const T* v_head,
+                                              size_t block_stride, int lane_off, int lane,
+                                              int row, int n_mine, int n_full, int tail_valid,
+                                              float scale_log2) {
   using G = Geometry<T, D, BS>;
-  constexpr int kVec = G::kVec;
-
-  const int part = blockIdx.x;
-  const int head = blockIdx.y;
-  const int seq = blockIdx.z;
-  const int ctx = prm.context_lens[seq];
-  const int P = prm.partition_tokens;
-  const int tok_begin = part * P;
-  T* out_row = static_cast<T*>(prm.out) + (static_cast<size_t>(seq) * prm.num_heads + head) * D;
-
-  if (tok_begin >= ctx) {
-    if (part == 0) {  // empty sequence: the output is zero
-      for (int d = threadIdx.x; d < D; d += kThreads) out_row[d] = Lane16<T>::from_float(0.0f);
-    }
-    return;
-  }
-  const int tok_end = min(ctx, tok_begin + P);
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const int row = lane / G::kLanesPerTok;
-  const int col = lane % G::kLanesPerTok;
-
-  const T* q_ptr = static_cast<const T*>(prm.query) +
-                   (static_cast<size_t>(seq) * prm.num_heads + head) * D + col * kVec;
-  const u32x4 q = load16(q_ptr);
-
-  const int* table = prm.block_tables + static_cast<size_t>(seq) * prm.max_blocks_per_seq;
-  const size_t block_stride = static_cast<size_t>(prm.num_heads) * BS * D;  // elements
-  const T* k_head = static_cast<const T*>(prm.key_cache) + static_cast<size_t>(head) * BS * D;
-  const T* v_head = static_cast<const T*>(prm.value_cache) + static_cast<size_t>(head) * BS * D;
-  const int lane_off = row * D + col * kVec;  // element offset of this lane in load 0
-
-  const int blk_begin = tok_begin / BS;  // P is a multiple of BS
-  const int full_end = tok_end / BS;     // blocks whose every token is live
-  const int blk_end = (tok_end + BS - 1) / BS;
-
-  RowState<kVec> st;
-  st.m = -INFINITY;
-  st.l = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kVec; ++j) st.acc[j] = 0.0f;
-
-  const float scale_log2 = prm.scale * kLog2e;
-
-  // This wave owns logical blocks blk_begin + wave + j * kWaves, j < n_mine; the
-  // last of them may be partly filled.  Their physical ids are fetched 64 at a time,
-  // one per lane, before any K/V load, and read back with readlane.
-  const int n_total = blk_end - blk_begin;
-  const int n_mine = n_total > wave ? (n_total - wave + kWaves - 1) / kWaves : 0;
-  const int n_full = full_end - blk_begin > wave ? (full_end - blk_begin - wave + kWaves - 1) / kWaves : 0;
-  const int* my_table = table + blk_begin + wave;
-
   for (int base = 0; base < n_mine; base += kWave) {
-    const int idx = base + lane;
-    const int ids = idx < n_mine ? my_table[idx * kWaves] : 0;
+    if (base > 0) {
+      const int idx = base + lane;
+      ids = idx < n_mine ? my_table[idx * kWaves] : 0;
+    }
     const int chunk_full = min(max(n_full - base, 0), kWave);
     int j = 0;
     // kUnroll full blocks per iteration, all loads issued before use
@@ -323,16 +290,81 @@ __global__ __launch_bounds__(kThreads) void decode_partitions_kernel(DecodeParam
       u32x4 kr[G::kLoads];
       u32x4 vr[G::kLoads];
       const int phys = __builtin_amdgcn_readlane(ids, j);
-      const int blk = blk_begin + wave + (base + j) * kWaves;
       const T* kp = k_head + static_cast<size_t>(phys) * block_stride + lane_off;
       const T* vp = v_head + static_cast<size_t>(phys) * block_stride + lane_off;
 #pragma unroll
       for (int i = 0; i < G::kLoads; ++i) kr[i] = load_kv16(kp + i * G::kTokPerLoad * D);
 #pragma unroll
       for (int i = 0; i < G::kLoads; ++i) vr[i] = load_kv16(vp + i * G::kTokPerLoad * D);
-      fold_block<T, D, BS, true>(st, q, kr, vr, scale_log2, row, tok_end - blk * BS);
+      fold_block<T, D, BS, true>(st, q, kr, vr, scale_log2, row, tail_valid);
     }
   }
+}
+
+// ---------------------------------------------------------------------------------
+// decode, partition pass
+// grid (max partitions, heads, seqs), kThreads threads
+// ---------------------------------------------------------------------------------
+
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kernel(DecodeParams prm) {
+  using G = Geometry<T, D, BS>;
+  constexpr int kVec = G::kVec;
+
+  const int part = blockIdx.x;
+  const int head = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int P = prm.partition_tokens;
+  const int tok_begin = part * P;
+  const int blk_begin = tok_begin / BS;  // P is a multiple of BS
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int row = lane / G::kLanesPerTok;
+  const int col = lane % G::kLanesPerTok;
+
+  // Issued together, before anything waits on memory: the context length, the
+  // query row and the ids of this wave's first kWave blocks.  The ids are bounded
+  // by the table row, not by the context (entries past the context are read but
+  // never used), so the K/V stream waits on one dependent load instead of two.
+  const int* table = prm.block_tables + static_cast<size_t>(seq) * prm.max_blocks_per_seq;
+  const int* my_table = table + blk_begin + wave;
+  const int ids0 = blk_begin + wave + lane * kWaves < prm.max_blocks_per_seq ? my_table[lane * kWaves] : 0;
+  const u32x4 q = load16(static_cast<const T*>(prm.query) +
+                         (static_cast<size_t>(seq) * prm.num_heads + head) * D + col * kVec);
+  const int ctx = prm.context_lens[seq];
+  T* out_row = static_cast<T*>(prm.out) + (static_cast<size_t>(seq) * prm.num_heads + head) * D;
+
+  if (tok_begin >= ctx) {
+    if (part == 0) {  // empty sequence: the output is zero
+      for (int d = threadIdx.x; d < D; d += kThreads) out_row[d] = Lane16<T>::from_float(0.0f);
+    }
+    return;
+  }
+  const int tok_end = min(ctx, tok_begin + P);
+  const int full_end = tok_end / BS;  // blocks whose every token is live
+  const int blk_end = (tok_end + BS - 1) / BS;
+
+  const size_t block_stride = static_cast<size_t>(prm.num_heads) * BS * D;  // elements
+  const T* k_head = static_cast<const T*>(prm.key_cache) + static_cast<size_t>(head) * BS * D;
+  const T* v_head = static_cast<const T*>(prm.value_cache) + static_cast<size_t>(head) * BS * D;
+  const int lane_off = row * D + col * kVec;  // element offset of this lane in load 0
+  const float scale_log2 = prm.scale * kLog2e;
+
+  // This wave owns logical blocks blk_begin + wave + j * kWaves, j < n_mine; the
+  // last of them may be partly filled.
+  const int n_total = blk_end - blk_begin;
+  const int n_mine = n_total > wave ? (n_total - wave + kWaves - 1) / kWaves : 0;
+  const int n_full = full_end - blk_begin > wave ? (full_end - blk_begin - wave + kWaves - 1) / kWaves : 0;
+  const int tail_valid = tok_end - (blk_begin + wave + n_full * kWaves) * BS;
+
+  RowState<kVec> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) st.acc[j] = 0.0f;
+  attend_blocks<T, D, BS>(st, q, ids0, my_table, k_head, v_head, block_stride, lane_off, lane, row,
+                          n_mine, n_full, tail_valid, scale_log2);
 
   // merge the token rows of the wave (lanes with the same col)
 #pragma unroll
@@ -368,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void decode_partitions_kernel(DecodeParam
     float o = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = (s_m[w] == -INFINITY) ? 0.0f : exp2f(s_m[w] - m);
+      const float f = (s_m[w] == -INFINITY) ? 0.0f : fast_exp2(s_m[w] - m);
       l = l + s_l[w] * f;
       o = o + s_o[w][d] * f;
     }
@@ -405,7 +437,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(ReduceParams prm) {
   float l = 0.0f;
   float o = 0.0f;
   for (int p = 0; p < np; ++p) {
-    const float f = exp2f(prm.ws_m[base + p] - m);
+    const float f = fast_exp2(prm.ws_m[base + p] - m);
     l = l + prm.ws_l[base + p] * f;
     o = o + prm.ws_o[(base + p) * D + d] * f;
   }

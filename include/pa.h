@@ -39,8 +39,9 @@
  *      slot_mapping          int32 [num_tokens]; slot = block * block_size + offset.
  *                            A negative slot means "skip this row".
  *      block_pairs           int32 [num_pairs, 2] = (source block, destination block).
- *  * Supported shapes: head_dim in {64, 128}; block_size in {8, 16, 32};
- *    other values return PA_ERR_UNSUPPORTED.  K/V heads equal query heads.
+ *  * Supported shapes: head_dim in {64, 128}; block_size in {8, 16, 32}
+ *    (pa_decode_shared_prefix: fp16, block_size 16 or 32); other values return
+ *    PA_ERR_UNSUPPORTED.  K/V heads equal query heads.
  *  * Errors: argument checks run on the host before anything is enqueued and return
  *    a status; nothing aborts and no C++ exception crosses the ABI.  A failed launch
  *    returns PA_ERR_HIP.  The text of the last error of the calling thread is
@@ -214,6 +215,73 @@ pa_status pa_block_copy(void* key_cache, void* value_cache, const int32_t* block
                         int32_t num_pairs, int32_t num_heads, int32_t head_dim,
                         int32_t block_size, int32_t num_blocks, pa_dtype dtype,
                         void* stream);
+
+/*
+ * Shared-prefix decode.
+ *
+ * Sequences may share their leading blocks by reference count, e.g. the prompt of
+ * several samples drawn from it ([Reading vLLM] §2.2, PhysicalTokenBlock.ref_count;
+ * [vLLM basics] §2.3: sharing, and copy-on-write once a sharer writes).  Sharing
+ * changes where the numbers live, not the attention, so pa_decode_shared_prefix
+ * computes exactly what pa_decode computes (same definition, tolerances and output
+ * layout).  It differs in how it reads the cache: each shared block is read once per
+ * group for all of the group's queries, as small dense products on the matrix cores
+ * (fp16 operands, fp32 accumulation; the softmax weights enter as two fp16 terms so
+ * that no precision is lost to their rounding), and the tokens after the prefix are
+ * read per sequence as in pa_decode.  The partial softmax states are then merged.
+ *
+ * Groups are ranges of sequences:
+ *   group_starts   int32 [num_groups + 1], device: group g is sequences
+ *                  [group_starts[g], group_starts[g + 1]); non-decreasing, within
+ *                  [0, num_seqs]; ranges do not overlap.
+ *   prefix_lens    int32 [num_seqs], device: the number of leading tokens that
+ *                  sequence s shares with the rest of its group; a multiple of
+ *                  block_size, <= context_lens[s] and <= max_prefix_len; the same
+ *                  for every sequence of a group; 0 for a sequence in no group.
+ *                  For every sequence of group g, the first prefix_lens[s] /
+ *                  block_size entries of its block table equal those of sequence
+ *                  group_starts[g].
+ *   max_prefix_len host: >= every prefix_lens[s], a multiple of block_size.
+ *   max_suffix_len host: >= every context_lens[s] - prefix_lens[s].
+ * Both are <= max_blocks_per_seq * block_size, and every context_lens[s] is too.
+ * Groups of any size are accepted; a group's prefix is read once per 16 members.
+ * Built for PA_F16, head_dim in {64, 128} and block_size in {16, 32}; other values
+ * return PA_ERR_UNSUPPORTED.  partition_size applies to the tokens after the prefix
+ * (as in pa_decode, sized by max_suffix_len); prefix_partition_size is the number
+ * of prefix tokens one workgroup reads (0 = library choice, else a positive
+ * multiple of max(16, block_size)).  The contents above are caller preconditions
+ * (unchecked device data, as for pa_decode).
+ *
+ * Workspace (always needed when num_seqs > 0), float32, with NPp = prefix
+ * partitions, NPs = partitions after the prefix and NS = NPp + NPs:
+ *     m [num_seqs, num_heads, NS]   at byte 0
+ *     l [num_seqs, num_heads, NS]   at byte ws_align(S*H*NS*4)
+ *     o [num_seqs, num_heads, NS, head_dim]   at byte 2*ws_align(S*H*NS*4)
+ * Slot p < NPp holds the state of prefix tokens [p*Pp, (p+1)*Pp) and slot NPp + p
+ * that of tokens [prefix_lens[s] + p*P, prefix_lens[s] + (p+1)*P), with the same
+ * (m, l, o) definition as pa_decode's workspace.  Slots past a sequence's tokens are
+ * not written, nor are the slots after the prefix of a sequence whose remaining
+ * tokens fit one partition: that partition's workgroup merges the prefix states and
+ * writes the output itself (the merge pass runs only when NPs > 1).  pa_decode_shared_prefix_workspace_bytes returns the size (0 and the
+ * last error set for invalid arguments).
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                               int32_t head_dim, int32_t block_size,
+                                               int32_t num_groups, int32_t max_prefix_len,
+                                               int32_t max_suffix_len,
+                                               int32_t partition_size,
+                                               int32_t prefix_partition_size);
+
+pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* group_starts,
+                                  const int32_t* prefix_lens, int32_t num_seqs,
+                                  int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, int32_t max_blocks_per_seq,
+                                  int32_t num_groups, int32_t max_prefix_len,
+                                  int32_t max_suffix_len, float scale, pa_dtype dtype,
+                                  int32_t partition_size, int32_t prefix_partition_size,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

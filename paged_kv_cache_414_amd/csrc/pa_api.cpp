@@ -39,8 +39,8 @@ pa_status from_hip(hipError_t err, const char* what) {
 // Library choice of the partition length: start from the whole longest context
 // (one partition per sequence, no merge pass) and halve while the launch would hold
 // fewer than kAutoMinUnits (sequence, head, partition) work units, i.e. about twelve
-// workgroups per compute unit of a 256-CU MI355X, never going below
-// kAutoMinPartitionTokens.  Measured on MI355X: long partitions stream at a higher
+// workgroups per compute unit of a 256-CU MI355X, as long as the half stays at or
+// above kAutoMinPartitionTokens.  Measured on MI355X: long partitions stream at a higher
 // rate (less per-workgroup set-up and fewer short tail partitions) as long as the
 // grid keeps every CU busy.
 constexpr int64_t kAutoMinUnits = 3072;
@@ -88,7 +88,8 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_heads, int32_t block_siz
     const int64_t units = pairs * ((static_cast<int64_t>(max_context_len) + P - 1) / P);
     if (units >= kAutoMinUnits) break;
     const int32_t half = round_up(P / 2, block_size);
-    P = half > floor_p ? half : floor_p;
+    if (half < floor_p) break;  // no short tail partitions below the floor
+    P = half;
   }
   return P;
 }
@@ -161,9 +162,85 @@ pa_status plan_decode(DecodePlan* plan, void* out, const void* query, const void
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
   p.max_blocks_per_seq = max_blocks_per_seq;
+  p.token_begin = nullptr;
   p.partition_tokens = P;
   p.num_partitions = NP;
+  p.slots_per_pair = NP;
+  p.slot_offset = 0;
+  p.prefix_partition_tokens = P;
   p.scale = scale;
+  return PA_OK;
+}
+
+// Library choice of the prefix partition length (tokens of the shared prefix that
+// one workgroup reads for all of a group's queries): the whole longest prefix,
+// halved while fewer than kPrefixMinUnits (group, head, partition) workgroups -- one
+// per compute unit -- would be launched, as long as the half stays at or above
+// kPrefixMinTokens.  Measured on MI355X (8 groups x 32 heads, 1024 shared tokens):
+// one partition per (group, head) beats 2, 4 and 8 (76.6, 79.3, 81, 93 us).
+constexpr int64_t kPrefixMinUnits = 256;
+constexpr int32_t kPrefixMinTokens = 64;
+constexpr int32_t kPrefixTile = 16;  // tokens per matrix-core tile of the prefix pass
+
+int32_t resolve_prefix_partition(int32_t num_groups, int32_t num_heads, int32_t block_size,
+                                 int32_t max_prefix_len, int32_t prefix_partition_size) {
+  const int32_t unit = block_size > kPrefixTile ? block_size : kPrefixTile;
+  if (prefix_partition_size < 0 || (prefix_partition_size > 0 && prefix_partition_size % unit != 0)) {
+    fail(PA_ERR_INVALID_ARG, "prefix_partition_size %d must be 0 or a positive multiple of %d",
+         prefix_partition_size, unit);
+    return -1;
+  }
+  if (prefix_partition_size > 0) return prefix_partition_size;
+  const int64_t pairs = static_cast<int64_t>(num_groups > 0 ? num_groups : 1) * (num_heads > 0 ? num_heads : 1);
+  const int32_t floor_p = round_up(kPrefixMinTokens, unit);
+  int32_t P = round_up(max_prefix_len > 0 ? max_prefix_len : 1, unit);
+  while (P > floor_p) {
+    const int64_t units = pairs * ((static_cast<int64_t>(max_prefix_len) + P - 1) / P);
+    if (units >= kPrefixMinUnits) break;
+    const int32_t half = round_up(P / 2, unit);
+    if (half < floor_p) break;
+    P = half;
+  }
+  return P;
+}
+
+struct SharedPlan {
+  int32_t Pp, NPp;  // prefix pass
+  int32_t P, NPs;   // pass over the tokens after the prefix
+  int32_t slots;    // NPp + NPs states per (sequence, head)
+  size_t ws_bytes;
+};
+
+pa_status plan_shared(SharedPlan* plan, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_groups, int32_t max_prefix_len,
+                      int32_t max_suffix_len, int32_t partition_size,
+                      int32_t prefix_partition_size) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 128)", head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not built for the shared-prefix decode (16, 32)",
+                block_size);
+  if (num_seqs < 0 || num_heads <= 0 || num_groups < 0)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs %d >= 0, num_heads %d > 0, num_groups %d >= 0 required",
+                num_seqs, num_heads, num_groups);
+  if (num_seqs > kMaxGridYZ || num_heads > kMaxGridYZ || num_groups > kMaxGridYZ)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs, num_heads and num_groups must be <= %d", kMaxGridYZ);
+  if (max_prefix_len < 0 || max_prefix_len % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, "max_prefix_len %d must be a non-negative multiple of block_size %d",
+                max_prefix_len, block_size);
+  if (max_suffix_len < 0) return fail(PA_ERR_INVALID_ARG, "max_suffix_len %d is negative", max_suffix_len);
+  const int32_t Pp = resolve_prefix_partition(num_groups, num_heads, block_size, max_prefix_len,
+                                              prefix_partition_size);
+  if (Pp < 0) return PA_ERR_INVALID_ARG;
+  const int32_t P = resolve_partition(num_seqs, num_heads, block_size, max_suffix_len, partition_size);
+  if (P < 0) return PA_ERR_INVALID_ARG;
+  plan->Pp = Pp;
+  plan->NPp = max_prefix_len > 0 ? partitions_for(max_prefix_len, Pp) : 0;
+  plan->P = P;
+  plan->NPs = partitions_for(max_suffix_len, P);
+  plan->slots = plan->NPp + plan->NPs;
+  const size_t states = static_cast<size_t>(num_seqs) * num_heads * plan->slots;
+  plan->ws_bytes = num_seqs > 0 ? 2 * ws_align(states * 4) + ws_align(states * head_dim * 4) : 0;
   return PA_OK;
 }
 
@@ -257,10 +334,13 @@ pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_by
   prm.ws_l = reinterpret_cast<const float*>(ws + ws_align(states * 4));
   prm.ws_o = reinterpret_cast<const float*>(ws + 2 * ws_align(states * 4));
   prm.context_lens = context_lens;
+  prm.prefix_lens = nullptr;
   prm.num_seqs = num_seqs;
   prm.num_heads = num_heads;
   prm.partition_tokens = P;
-  prm.num_partitions = NP;
+  prm.prefix_partition_tokens = P;
+  prm.prefix_slots = 0;
+  prm.slots_per_pair = NP;
   return from_hip(pa::launch_decode_reduce(prm, dtype == PA_F16, head_dim, static_cast<hipStream_t>(stream)),
                   "decode reduce pass launch");
 }
@@ -334,4 +414,121 @@ pa_status pa_block_copy(void* key_cache, void* value_cache, const int32_t* block
   return from_hip(pa::launch_block_copy(prm, static_cast<hipStream_t>(stream)), "block copy launch");
 }
 
-}  // extern "C"
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t num_groups,
+                                               int32_t max_prefix_len, int32_t max_suffix_len,
+                                               int32_t partition_size, int32_t prefix_partition_size) {
+  SharedPlan plan;
+  if (plan_shared(&plan, num_seqs, num_heads, head_dim, block_size, num_groups, max_prefix_len,
+                  max_suffix_len, partition_size, prefix_partition_size) != PA_OK)
+    return 0;
+  return plan.ws_bytes;
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* group_starts,
+                                  const int32_t* prefix_lens, int32_t num_seqs, int32_t num_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t num_groups,
+                                  int32_t max_prefix_len, int32_t max_suffix_len, float scale,
+                                  pa_dtype dtype, int32_t partition_size,
+                                  int32_t prefix_partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "the shared-prefix decode is built for PA_F16 only (dtype %d)", (int)dtype);
+  SharedPlan plan;
+  pa_status st = plan_shared(&plan, num_seqs, num_heads, head_dim, block_size, num_groups, max_prefix_len,
+                             max_suffix_len, partition_size, prefix_partition_size);
+  if (st != PA_OK) return st;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks %d and max_blocks_per_seq %d must be positive", num_blocks,
+                max_blocks_per_seq);
+  const int64_t row_tokens = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  if (max_prefix_len > row_tokens || max_suffix_len > row_tokens)
+    return fail(PA_ERR_INVALID_ARG, "max_prefix_len %d and max_suffix_len %d must be <= max_blocks_per_seq * block_size = %lld",
+                max_prefix_len, max_suffix_len, static_cast<long long>(row_tokens));
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (num_seqs == 0) return ok();
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens || !prefix_lens ||
+      (num_groups > 0 && !group_starts))
+    return fail(PA_ERR_NULL, "a required pointer is NULL (out, query, key_cache, value_cache, block_tables, "
+                             "context_lens, prefix_lens, group_starts)");
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_ERR_INVALID_ARG, "out, query and the caches must be 16-byte aligned");
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", plan.ws_bytes);
+  if (workspace_bytes < plan.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.ws_bytes);
+  if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  const size_t states = static_cast<size_t>(num_seqs) * num_heads * plan.slots;
+  char* ws = static_cast<char*>(workspace);
+  float* ws_m = reinterpret_cast<float*>(ws);
+  float* ws_l = reinterpret_cast<float*>(ws + ws_align(states * 4));
+  float* ws_o = reinterpret_cast<float*>(ws + 2 * ws_align(states * 4));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  if (num_groups > 0 && plan.NPp > 0) {
+    pa::PrefixParams pp;
+    pp.query = query;
+    pp.key_cache = key_cache;
+    pp.value_cache = value_cache;
+    pp.block_tables = block_tables;
+    pp.group_starts = group_starts;
+    pp.prefix_lens = prefix_lens;
+    pp.ws_m = ws_m;
+    pp.ws_l = ws_l;
+    pp.ws_o = ws_o;
+    pp.num_heads = num_heads;
+    pp.max_blocks_per_seq = max_blocks_per_seq;
+    pp.partition_tokens = plan.Pp;
+    pp.num_partitions = plan.NPp;
+    pp.num_groups = num_groups;
+    pp.slots_per_pair = plan.slots;
+    pp.scale = scale;
+    st = from_hip(pa::launch_decode_prefix(pp, head_dim, block_size, hs), "shared-prefix pass launch");
+    if (st != PA_OK) return st;
+  }
+
+  pa::DecodeParams dp;
+  dp.out = out;
+  dp.query = query;
+  dp.key_cache = key_cache;
+  dp.value_cache = value_cache;
+  dp.block_tables = block_tables;
+  dp.context_lens = context_lens;
+  dp.token_begin = prefix_lens;
+  dp.ws_m = ws_m;
+  dp.ws_l = ws_l;
+  dp.ws_o = ws_o;
+  dp.num_seqs = num_seqs;
+  dp.num_heads = num_heads;
+  dp.max_blocks_per_seq = max_blocks_per_seq;
+  dp.partition_tokens = plan.P;
+  dp.num_partitions = plan.NPs;
+  dp.slots_per_pair = plan.slots;
+  dp.slot_offset = plan.NPp;
+  dp.prefix_partition_tokens = plan.Pp;
+  dp.scale = scale;
+  st = from_hip(pa::launch_decode_partitions(dp, true, head_dim, block_size, hs), "suffix pass launch");
+  if (st != PA_OK) return st;
+  // sequences whose tokens after the prefix fit one partition are finished above
+  if (plan.NPs <= 1) return ok();
+
+  pa::ReduceParams rp;
+  rp.out = out;
+  rp.ws_m = ws_m;
+  rp.ws_l = ws_l;
+  rp.ws_o = ws_o;
+  rp.context_lens = context_lens;
+  rp.prefix_lens = prefix_lens;
+  rp.num_seqs = num_seqs;
+  rp.num_heads = num_heads;
+  rp.partition_tokens = plan.P;
+  rp.prefix_partition_tokens = plan.Pp;
+  rp.prefix_slots = plan.NPp;
+  rp.slots_per_pair = plan.slots;
+  return from_hip(pa::launch_decode_reduce(rp, true, head_dim, hs), "shared-prefix merge launch");
+}
+
+}  // extern "C\"

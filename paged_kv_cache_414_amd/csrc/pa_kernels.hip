@@ -301,6 +301,25 @@ __device__ __forceinline__ void attend_blocks(RowState<Geometry<T, D, BS>::kVec>
   }
 }
 
+// Fold the prefix states of (seq, head) -- partitions of the first `start` tokens,
+// left in the workspace by the prefix pass -- into the state (m, l, o) of dim d.
+__device__ __forceinline__ void fold_prefix_states(const DecodeParams& prm, int seq, int head,
+                                                   int start, int d, int D, float& m, float& l,
+                                                   float& o) {
+  const int Pp = prm.prefix_partition_tokens;
+  const int np_prefix = (start + Pp - 1) / Pp;
+  const size_t base = (static_cast<size_t>(seq) * prm.num_heads + head) * prm.slots_per_pair;
+  for (int p = 0; p < np_prefix; ++p) {
+    const float mp = prm.ws_m[base + p];
+    const float mm = fmaxf(m, mp);
+    const float fa = (m == -INFINITY) ? 0.0f : fast_exp2(m - mm);
+    const float fb = fast_exp2(mp - mm);
+    l = l * fa + prm.ws_l[base + p] * fb;
+    o = o * fa + prm.ws_o[(base + p) * D + d] * fb;
+    m = mm;
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // decode, partition pass
 // grid (max partitions, heads, seqs), kThreads threads
@@ -315,7 +334,8 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
   const int head = blockIdx.y;
   const int seq = blockIdx.z;
   const int P = prm.partition_tokens;
-  const int tok_begin = part * P;
+  const int start = prm.token_begin ? prm.token_begin[seq] : 0;  // a multiple of BS
+  const int tok_begin = start + part * P;
   const int blk_begin = tok_begin / BS;  // P is a multiple of BS
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -336,8 +356,12 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
   T* out_row = static_cast<T*>(prm.out) + (static_cast<size_t>(seq) * prm.num_heads + head) * D;
 
   if (tok_begin >= ctx) {
-    if (part == 0) {  // empty sequence: the output is zero
-      for (int d = threadIdx.x; d < D; d += kThreads) out_row[d] = Lane16<T>::from_float(0.0f);
+    if (part == 0) {  // no token after `start`: the prefix states alone, or zero
+      for (int d = threadIdx.x; d < D; d += kThreads) {
+        float m = -INFINITY, l = 0.0f, o = 0.0f;
+        if (start > 0) fold_prefix_states(prm, seq, head, start, d, D, m, l, o);
+        out_row[d] = Lane16<T>::from_float(l > 0.0f ? o / l : 0.0f);
+      }
     }
     return;
   }
@@ -391,7 +415,9 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
   }
   __syncthreads();
 
-  const bool single = ctx <= P;
+  // one partition covers every token after `start`: finish here (merging the
+  // prefix states, if any), no reduce pass needed for this sequence
+  const bool single = ctx - start <= P;
   for (int d = threadIdx.x; d < D; d += kThreads) {
     float m = s_m[0];
 #pragma unroll
@@ -405,9 +431,11 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
       o = o + s_o[w][d] * f;
     }
     if (single) {
+      if (start > 0) fold_prefix_states(prm, seq, head, start, d, D, m, l, o);
       out_row[d] = Lane16<T>::from_float(o / l);
     } else {
-      const size_t slot = (static_cast<size_t>(seq) * prm.num_heads + head) * prm.num_partitions + part;
+      const size_t slot = (static_cast<size_t>(seq) * prm.num_heads + head) * prm.slots_per_pair +
+                          prm.slot_offset + part;
       prm.ws_o[slot * D + d] = o;
       if (d == 0) {
         prm.ws_m[slot] = m;
@@ -426,23 +454,271 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(ReduceParams prm) {
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
   const int ctx = prm.context_lens[seq];
+  const int start = prm.prefix_lens ? prm.prefix_lens[seq] : 0;
   const int P = prm.partition_tokens;
-  const int np = (ctx + P - 1) / P;
-  if (np <= 1) return;  // written directly by the partition pass
+  const int Pp = prm.prefix_partition_tokens;
+  const int np_suffix = ctx > start ? (ctx - start + P - 1) / P : 0;
+  const int np_prefix = start > 0 ? (start + Pp - 1) / Pp : 0;
+  if (np_suffix <= 1) return;  // written directly by the partition pass
   const int d = threadIdx.x;
-  const size_t base = (static_cast<size_t>(seq) * prm.num_heads + head) * prm.num_partitions;
+  const size_t base = (static_cast<size_t>(seq) * prm.num_heads + head) * prm.slots_per_pair;
+  const size_t suffix = base + prm.prefix_slots;
 
+  // prefix states first, then the states after the prefix, each in token order
   float m = -INFINITY;
-  for (int p = 0; p < np; ++p) m = fmaxf(m, prm.ws_m[base + p]);
+  for (int p = 0; p < np_prefix; ++p) m = fmaxf(m, prm.ws_m[base + p]);
+  for (int p = 0; p < np_suffix; ++p) m = fmaxf(m, prm.ws_m[suffix + p]);
   float l = 0.0f;
   float o = 0.0f;
-  for (int p = 0; p < np; ++p) {
+  for (int p = 0; p < np_prefix; ++p) {
     const float f = fast_exp2(prm.ws_m[base + p] - m);
     l = l + prm.ws_l[base + p] * f;
     o = o + prm.ws_o[(base + p) * D + d] * f;
   }
+  for (int p = 0; p < np_suffix; ++p) {
+    const float f = fast_exp2(prm.ws_m[suffix + p] - m);
+    l = l + prm.ws_l[suffix + p] * f;
+    o = o + prm.ws_o[(suffix + p) * D + d] * f;
+  }
   T* out_row = static_cast<T*>(prm.out) + (static_cast<size_t>(seq) * prm.num_heads + head) * D;
   out_row[d] = Lane16<T>::from_float(o / l);
+}
+
+// ---------------------------------------------------------------------------------
+// decode, prefix pass of the shared-prefix decode (fp16): grid (prefix partitions,
+// heads, groups), kPrefixThreads threads.
+//
+// A group is a range of sequences whose first prefix_len tokens live in the same
+// physical blocks (shared by reference count).  Each shared block is read once for
+// all of the group's queries, so the score and value products become small dense
+// matrix products, run on the matrix cores as v_mfma_f32_16x16x16_f16 tiles of 16
+// tokens x 16 queries:
+//   scores  S^T[t][g] = sum_d K[t][d] Q[g][d]   (A = K tile, B = Q^T; lane l holds
+//           token l%16 of K and query l%16 of Q, both over the same dims)
+//   output  O^T[d][g] = sum_t V[t][d] P[g][t]   (A = V^T, B = P^T)
+// The matrix-core result layout puts tokens 4(l/16)..+3 of query l%16 in lane l,
+// which is exactly the B operand layout of the value product, so the softmax
+// weights never leave their lanes.  For the A operand of the value product the
+// output dims are relabelled (row m of tile dt is dim D/16*m + dt), so that every
+// lane loads its V rows as contiguous 16-byte runs.  The weights enter the value
+// product as two fp16 terms (p = hi + lo, hi = fp16(p), lo = fp16(p - hi)), which
+// keeps the products within fp32 rounding of the exact weights; accumulation is
+// fp32 throughout.  Each (partition, head, sequence) leaves its partial softmax
+// state in the workspace; the reduce pass merges it with the rest of the sequence.
+// ---------------------------------------------------------------------------------
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#ifndef PA_PREFIX_PREFETCH
+#define PA_PREFIX_PREFETCH 1  // 1: the prefix pass keeps the next tile's loads in flight
+#endif
+constexpr int kPrefixWaves = 4;
+constexpr int kPrefixThreads = kPrefixWaves * kWave;
+constexpr int kTile = 16;  // tokens and queries per matrix-core tile
+
+// One lane's run of kN fp16 values of a V row (kN = 8: 16 bytes, kN = 4: 8 bytes).
+template <int kN> struct HalfRun;
+template <> struct HalfRun<8> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const _Float16* p) { w = load_kv16(p); }
+  __device__ __forceinline__ _Float16 at(int i) const { return as_h2(w[i / 2])[i % 2]; }
+};
+template <> struct HalfRun<4> {
+  u32x2 w;
+  __device__ __forceinline__ void load(const _Float16* p) {
+    w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  }
+  __device__ __forceinline__ _Float16 at(int i) const { return as_h2(w[i / 2])[i % 2]; }
+};
+
+template <int D, int BS>
+__global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixParams prm) {
+  static_assert(BS % kTile == 0 && (D == 64 || D == 128), "shape");
+  constexpr int kTilesPerBlock = BS / kTile;
+  constexpr int kDq = D / 4;          // dims per lane in the score product
+  constexpr int kQLoads = kDq / 8;    // 16-byte loads of them
+  constexpr int kSteps = D / 16;      // score-product matrix-core steps over the dims
+  constexpr int kDv = D / 16;         // dims per lane per V row, also value-product tiles
+
+  const int part = blockIdx.x;
+  const int head = blockIdx.y;
+  const int grp = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int c16 = lane % kTile;  // K row and query column of this lane
+  const int j = lane / kTile;    // lane group
+
+  const int s0 = prm.group_starts[grp];
+  const int n_seqs = prm.group_starts[grp + 1] - s0;
+  if (n_seqs <= 0) return;
+  const int plen = prm.prefix_lens[s0];
+  const int P = prm.partition_tokens;
+  const int tok_begin = part * P;
+  if (tok_begin >= plen) return;
+  const int tok_end = min(plen, tok_begin + P);  // plen is a whole number of tiles
+  const int tile_begin = tok_begin / kTile;
+  const int n_tiles = (tok_end - tok_begin) / kTile;
+  const int n_mine = n_tiles > wave ? (n_tiles - wave + kPrefixWaves - 1) / kPrefixWaves : 0;
+
+  const int* table = prm.block_tables + static_cast<size_t>(s0) * prm.max_blocks_per_seq;
+  const size_t block_stride = static_cast<size_t>(prm.num_heads) * BS * D;  // elements
+  const _Float16* k_head = static_cast<const _Float16*>(prm.key_cache) + static_cast<size_t>(head) * BS * D;
+  const _Float16* v_head = static_cast<const _Float16*>(prm.value_cache) + static_cast<size_t>(head) * BS * D;
+  const float scale_log2 = prm.scale * kLog2e;
+
+  __shared__ float s_m[kPrefixWaves][kTile];
+  __shared__ float s_l[kPrefixWaves][kTile];
+  __shared__ float s_o[kPrefixWaves][kTile][D + 1];  // +1: rows of one lane group hit distinct banks
+
+  for (int q0 = 0; q0 < n_seqs; q0 += kTile) {
+    // B operand of the score product: query q0 + c16, dims [kDq*j, kDq*j + kDq)
+    u32x4 qv[kQLoads];
+    if (q0 + c16 < n_seqs) {
+      const _Float16* qp = static_cast<const _Float16*>(prm.query) +
+                           (static_cast<size_t>(s0 + q0 + c16) * prm.num_heads + head) * D + kDq * j;
+#pragma unroll
+      for (int i = 0; i < kQLoads; ++i) qv[i] = load16(qp + 8 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kQLoads; ++i) qv[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    float m = -INFINITY;  // running max (base 2) of query c16
+    float l = 0.0f;
+    f32x4 acc[kDv];       // acc[dt][v] = O[c16][kDv * (4j + v) + dt]
+#pragma unroll
+    for (int dt = 0; dt < kDv; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Fold one tile (scores, online softmax, value product) into the state.
+    auto fold_tile = [&](const u32x4 (&kv)[kQLoads], const HalfRun<kDv> (&vr)[4]) {
+      // scores: sc[v] = <K row 4j+v, query c16>
+      f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < kSteps; ++c) {
+        const u32x2 a = {kv[c / 2][2 * (c % 2)], kv[c / 2][2 * (c % 2) + 1]};
+        const u32x2 b = {qv[c / 2][2 * (c % 2)], qv[c / 2][2 * (c % 2) + 1]};
+        sc = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                   __builtin_bit_cast(f16x4, b), sc, 0, 0, 0);
+      }
+      // online softmax of query c16 over the tile's 16 tokens (4 per lane group)
+      float z[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) z[v] = sc[v] * scale_log2;
+      float top = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      top = fmaxf(top, __shfl_xor(top, 16));
+      top = fmaxf(top, __shfl_xor(top, 32));
+      const float m_new = fmaxf(m, top);
+      const float alpha = fast_exp2(m - m_new);  // 0 before the first tile
+      float p[4];
+      float psum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        p[v] = fast_exp2(z[v] - m_new);
+        psum += p[v];
+      }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      l = l * alpha + psum;
+      m = m_new;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int dt = 0; dt < kDv; ++dt) acc[dt] *= alpha;
+      }
+      // value product: B = P^T (token 4j+v, query c16) as hi + lo fp16 terms
+      f16x4 p_hi, p_lo;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        p_hi[v] = static_cast<_Float16>(p[v]);
+        p_lo[v] = static_cast<_Float16>(p[v] - static_cast<float>(p_hi[v]));
+      }
+#pragma unroll
+      for (int dt = 0; dt < kDv; ++dt) {
+        const f16x4 a = {vr[0].at(dt), vr[1].at(dt), vr[2].at(dt), vr[3].at(dt)};
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, p_hi, acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, p_lo, acc[dt], 0, 0, 0);
+      }
+    };
+
+    for (int base = 0; base < n_mine; base += kWave) {
+      // physical block of each of this wave's tiles, one per lane
+      const int idx = base + lane;
+      const int ids = idx < n_mine
+                          ? table[(tile_begin + wave + idx * kPrefixWaves) / kTilesPerBlock]
+                          : 0;
+      const int n_here = min(n_mine - base, kWave);
+      // K row c16 (dims [kDq*j, kDq*j + kDq)) and V rows 4j+v (dims [kDv*c16, +kDv))
+      // of the wave's i-th tile of this chunk
+      auto load_tile = [&](int i, u32x4 (&kv)[kQLoads], HalfRun<kDv> (&vr)[4]) {
+        const int tile = tile_begin + wave + (base + i) * kPrefixWaves;
+        const int phys = __builtin_amdgcn_readlane(ids, i);
+        const size_t off = static_cast<size_t>(phys) * block_stride +
+                           static_cast<size_t>(tile % kTilesPerBlock) * kTile * D;
+#pragma unroll
+        for (int ii = 0; ii < kQLoads; ++ii) kv[ii] = load_kv16(k_head + off + c16 * D + kDq * j + 8 * ii);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) vr[v].load(v_head + off + (4 * j + v) * D + kDv * c16);
+      };
+#if PA_PREFIX_PREFETCH
+      // two tiles in registers: the next tile's loads are in flight while the
+      // current one is folded
+      u32x4 ka[kQLoads], kb[kQLoads];
+      HalfRun<kDv> va[4], vb[4];
+      int i = 0;
+      load_tile(0, ka, va);
+      for (; i + 1 < n_here; i += 2) {
+        load_tile(i + 1, kb, vb);
+        fold_tile(ka, va);
+        if (i + 2 < n_here) load_tile(i + 2, ka, va);
+        fold_tile(kb, vb);
+      }
+      if (i < n_here) fold_tile(ka, va);
+#else
+      for (int i = 0; i < n_here; ++i) {
+        u32x4 kv[kQLoads];
+        HalfRun<kDv> vr[4];
+        load_tile(i, kv, vr);
+        fold_tile(kv, vr);
+      }
+#endif
+    }
+
+    // merge the waves through LDS and leave one state per (sequence, head, partition)
+    if (j == 0) {
+      s_m[wave][c16] = m;
+      s_l[wave][c16] = l;
+    }
+#pragma unroll
+    for (int dt = 0; dt < kDv; ++dt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_o[wave][c16][kDv * (4 * j + v) + dt] = acc[dt][v];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < kTile * D; e += kPrefixThreads) {
+      const int g = e / D;
+      const int d = e % D;
+      if (q0 + g >= n_seqs) break;  // e grows with g
+      float mm = s_m[0][g];
+#pragma unroll
+      for (int w = 1; w < kPrefixWaves; ++w) mm = fmaxf(mm, s_m[w][g]);
+      float ll = 0.0f;
+      float oo = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kPrefixWaves; ++w) {
+        const float f = (s_m[w][g] == -INFINITY) ? 0.0f : fast_exp2(s_m[w][g] - mm);
+        ll = ll + s_l[w][g] * f;
+        oo = oo + s_o[w][g][d] * f;
+      }
+      const size_t slot = (static_cast<size_t>(s0 + q0 + g) * prm.num_heads + head) * prm.slots_per_pair + part;
+      prm.ws_o[slot * D + d] = oo;
+      if (d == 0) {
+        prm.ws_m[slot] = mm;
+        prm.ws_l[slot] = ll;
+      }
+    }
+    __syncthreads();  // the LDS arrays are reused by the next tile of queries
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -549,6 +825,31 @@ static hipError_t launch_reduce_t(const ReduceParams& prm, int head_dim, hipStre
 hipError_t launch_decode_reduce(const ReduceParams& prm, bool f16, int head_dim, hipStream_t stream) {
   return f16 ? launch_reduce_t<_Float16>(prm, head_dim, stream)
              : launch_reduce_t<float>(prm, head_dim, stream);
+}
+
+template <int D>
+static hipError_t launch_prefix_d(const PrefixParams& prm, int block_size, hipStream_t stream) {
+  dim3 grid(prm.num_partitions, prm.num_heads, prm.num_groups);
+  switch (block_size) {
+    case 16:
+      hipLaunchKernelGGL((decode_prefix_kernel<D, 16>), grid, dim3(kPrefixThreads), 0, stream, prm);
+      break;
+    case 32:
+      hipLaunchKernelGGL((decode_prefix_kernel<D, 32>), grid, dim3(kPrefixThreads), 0, stream, prm);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_prefix(const PrefixParams& prm, int head_dim, int block_size,
+                                hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_prefix_d<64>(prm, block_size, stream);
+    case 128: return launch_prefix_d<128>(prm, block_size, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_cache_append(const AppendParams& prm, hipStream_t stream) {

@@ -15,14 +15,39 @@ struct DecodeParams {
   const void* value_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_m;  // [S, H, NP]
-  float* ws_l;  // [S, H, NP]
-  float* ws_o;  // [S, H, NP, D]
+  const int32_t* token_begin;  // [S] first token of each sequence to attend, or nullptr (= 0)
+  float* ws_m;  // [S, H, slots_per_pair]
+  float* ws_l;  // [S, H, slots_per_pair]
+  float* ws_o;  // [S, H, slots_per_pair, D]
   int32_t num_seqs;
   int32_t num_heads;
   int32_t max_blocks_per_seq;
   int32_t partition_tokens;  // P, a multiple of the block size
-  int32_t num_partitions;    // NP reserved per (seq, head) = grid.x
+  int32_t num_partitions;    // partitions launched per (seq, head) = grid.x
+  int32_t slots_per_pair;    // partial-state slots reserved per (seq, head)
+  int32_t slot_offset;       // slot of partition 0 of this pass (= prefix slots)
+  int32_t prefix_partition_tokens;  // with token_begin: the prefix states' partition length
+  float scale;
+};
+
+// Prefix pass of the shared-prefix decode: one workgroup per (prefix partition,
+// head, group); groups are ranges of sequences that share leading blocks.
+struct PrefixParams {
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* group_starts;  // [G + 1]
+  const int32_t* prefix_lens;   // [S]
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+  int32_t num_heads;
+  int32_t max_blocks_per_seq;
+  int32_t partition_tokens;  // a multiple of 16 and of the block size
+  int32_t num_partitions;    // grid.x
+  int32_t num_groups;        // grid.z
+  int32_t slots_per_pair;
   float scale;
 };
 
@@ -32,10 +57,13 @@ struct ReduceParams {
   const float* ws_l;
   const float* ws_o;
   const int32_t* context_lens;
+  const int32_t* prefix_lens;  // [S] tokens covered by the prefix pass, or nullptr
   int32_t num_seqs;
   int32_t num_heads;
-  int32_t partition_tokens;
-  int32_t num_partitions;
+  int32_t partition_tokens;         // of the states after the prefix
+  int32_t prefix_partition_tokens;  // of the prefix states
+  int32_t prefix_slots;             // slots [0, prefix_slots) hold prefix states
+  int32_t slots_per_pair;
 };
 
 struct AppendParams {
@@ -61,6 +89,8 @@ struct CopyParams {
 hipError_t launch_decode_partitions(const DecodeParams& prm, bool f16, int head_dim,
                                     int block_size, hipStream_t stream);
 hipError_t launch_decode_reduce(const ReduceParams& prm, bool f16, int head_dim,
+                                hipStream_t stream);
+hipError_t launch_decode_prefix(const PrefixParams& prm, int head_dim, int block_size,
                                 hipStream_t stream);
 hipError_t launch_cache_append(const AppendParams& prm, hipStream_t stream);
 hipError_t launch_block_copy(const CopyParams& prm, hipStream_t stream);

@@ -40,6 +40,9 @@ SIGNATURES = {
     "pa_cache_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                _vp]),
     "pa_block_copy": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32] * 9),
+    "pa_decode_shared_prefix": (_i32, [_vp] * 8 + [_i32] * 9 + [_f32, _i32, _i32, _i32, _vp,
+                                                                _sz, _vp]),
 }
 
 
@@ -228,3 +231,58 @@ def pa_block_copy(key_cache, value_cache, block_pairs, stream=None):
     _check(lib.pa_block_copy(_ptr(key_cache), _ptr(value_cache), _ptr(block_pairs),
                              block_pairs.shape[0], h, d, bs, nb, _dtype(key_cache),
                              _stream(stream, dev)))
+
+
+# ----------------------------------------------------------------------------------
+# shared-prefix decode
+# ----------------------------------------------------------------------------------
+
+def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_heads, head_dim, block_size,
+                                            num_groups, max_prefix_len, max_suffix_len,
+                                            partition_size=0, prefix_partition_size=0) -> int:
+    n = int(lib.pa_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_heads, head_dim, block_size, num_groups, max_prefix_len,
+        max_suffix_len, partition_size, prefix_partition_size))
+    if n == 0 and num_seqs > 0:
+        raise PagedAttentionError(2, lib.pa_last_error().decode())
+    return n
+
+
+def shared_prefix_workspace_for(query, key_cache, num_groups, max_prefix_len,
+                                max_suffix_len, partition_size=0,
+                                prefix_partition_size=0) -> torch.Tensor | None:
+    """Device buffer of the size pa_decode_shared_prefix needs."""
+    s, h, d = query.shape
+    n = pa_decode_shared_prefix_workspace_bytes(s, h, d, key_cache.shape[2], num_groups,
+                                                max_prefix_len, max_suffix_len,
+                                                partition_size, prefix_partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=query.device)
+
+
+def pa_decode_shared_prefix(out, query, key_cache, value_cache, block_tables, context_lens,
+                            group_starts, prefix_lens, scale, max_prefix_len, max_suffix_len,
+                            partition_size=0, prefix_partition_size=0, workspace=None,
+                            stream=None):
+    """pa_decode for groups of sequences that share leading blocks (see include/pa.h).
+
+    group_starts int32 [G + 1] and prefix_lens int32 [S] describe the groups."""
+    args = list(_decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                             scale, 0, partition_size, workspace, stream))
+    dev = _same_device(out, group_starts, prefix_lens)
+    _int32(group_starts, prefix_lens)
+    s = query.shape[0]
+    if group_starts.dim() != 1 or prefix_lens.shape != (s,):
+        raise ValueError("group_starts must be [G + 1] and prefix_lens [S]")
+    num_groups = group_starts.shape[0] - 1
+    if num_groups < 0:
+        raise ValueError("group_starts needs at least one entry")
+    (p_out, p_q, p_k, p_v, p_bt, p_ctx, s, h, d, bs, nb, mb, _mcl, scale_f, dt, part, p_ws,
+     ws_bytes, strm) = args
+    _check(lib.pa_decode_shared_prefix(p_out, p_q, p_k, p_v, p_bt, p_ctx, _ptr(group_starts),
+                                       _ptr(prefix_lens), s, h, d, bs, nb, mb, num_groups,
+                                       int(max_prefix_len), int(max_suffix_len), scale_f, dt,
+                                       part, int(prefix_partition_size), p_ws, ws_bytes,
+                                       _stream(stream, dev) if stream is not None else strm))
+    return out

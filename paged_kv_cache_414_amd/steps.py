@@ -174,20 +174,25 @@ class StepMix:
         self._append_rows(slots, inp.new_k, inp.new_v, nk_d, nv_d)
         q_d = self.to_dev(inp.q) if q_d is None else q_d
         tables_d, ctx_d = self.to_dev(tables), self.to_dev(ctx)
-        ws = self._workspace(q_d, max_ctx)
-        ops.pa_decode(self.out, q_d, self.k_cache, self.v_cache, tables_d, ctx_d, self.scale,
-                      max_ctx, 0, ws)
-        self.last_decode = (q_d, tables_d, ctx_d, max_ctx, ws)
+        self.last_decode = self._decode_call(q_d, tables, tables_d, ctx, ctx_d, max_ctx)
+        self.last_decode()
         if self.keep:
             self.records.append(StepRecord(k_step, pairs, slots, inp.new_k, inp.new_v,
                                            np.array(positions), tables, ctx, inp.q))
         return ctx
 
+    def _decode_call(self, q_d, tables, tables_d, ctx, ctx_d, max_ctx):
+        """The step's decode as a callable (enqueued once per step; again for timing)."""
+        ws = self._workspace(q_d, max_ctx)
+
+        def call():
+            ops.pa_decode(self.out, q_d, self.k_cache, self.v_cache, tables_d, ctx_d,
+                          self.scale, max_ctx, 0, ws)
+        return call
+
     def decode_again(self):
         """Enqueue the last step's decode once more (same inputs; for timing)."""
-        q_d, tables_d, ctx_d, max_ctx, ws = self.last_decode
-        ops.pa_decode(self.out, q_d, self.k_cache, self.v_cache, tables_d, ctx_d, self.scale,
-                      max_ctx, 0, ws)
+        self.last_decode()
 
     def kv_bytes(self, ctx) -> int:
         return metrics.decode_kv_bytes(ctx, self.spec.num_heads, self.spec.head_dim,
@@ -233,10 +238,16 @@ class ContinuousBatching(StepMix):
 
 
 class SharedPrefix(StepMix):
-    """8 groups x 8 samples sharing their prompt blocks (see module docstring)."""
+    """8 groups x 8 samples sharing their prompt blocks (see module docstring).
+
+    With ``shared_decode`` the decode runs through pa_decode_shared_prefix: each
+    group's leading blocks that all of its samples still hold are read once for the
+    whole group."""
 
     def __init__(self, seed: int, steps: int | None = None, device="cuda",
-                 keep_records=False):
+                 keep_records=False, shared_decode=False):
+        self.shared_decode = bool(shared_decode)
+        self.ws_shared = None
         spec = workloads.SHARED_PREFIX
         draws = workloads.SharedPrefixDraws(spec, seed)
         steps = steps or spec.steps
@@ -253,6 +264,41 @@ class SharedPrefix(StepMix):
                 group.append(child)
             self.lanes.extend(group)
         self.initial = (slots, k, v)
+
+    def shared_prefix(self, tables: np.ndarray, ctx: np.ndarray):
+        """(group_starts, prefix_lens): the lanes of a group are contiguous; its
+        prefix is the leading whole blocks whose ids every member's table holds."""
+        n = self.draws.samples
+        starts = np.arange(0, len(self.lanes) + 1, n, dtype=np.int32)
+        prefix = np.zeros(len(self.lanes), dtype=np.int32)
+        bs = self.spec.block_size
+        for r0 in starts[:-1]:
+            rows = tables[r0:r0 + n]
+            same = np.all(rows == rows[0], axis=0)
+            lead = int(np.argmin(same)) if not same.all() else same.size
+            lead = min(lead, int(ctx[r0:r0 + n].min()) // bs)
+            prefix[r0:r0 + n] = lead * bs
+        return starts, prefix
+
+    def _decode_call(self, q_d, tables, tables_d, ctx, ctx_d, max_ctx):
+        if not self.shared_decode:
+            return super()._decode_call(q_d, tables, tables_d, ctx, ctx_d, max_ctx)
+        starts, prefix = self.shared_prefix(tables, ctx)
+        max_prefix = int(prefix.max())
+        max_suffix = int((ctx - prefix).max())
+        starts_d, prefix_d = self.to_dev(starts), self.to_dev(prefix)
+        need = ops.pa_decode_shared_prefix_workspace_bytes(
+            q_d.shape[0], q_d.shape[1], q_d.shape[2], self.spec.block_size, len(starts) - 1,
+            max_prefix, max_suffix)
+        if self.ws_shared is None or self.ws_shared.numel() < need:
+            self.ws_shared = torch.empty(need, dtype=torch.uint8, device=self.device)
+        ws = self.ws_shared
+
+        def call():
+            ops.pa_decode_shared_prefix(self.out, q_d, self.k_cache, self.v_cache, tables_d,
+                                        ctx_d, starts_d, prefix_d, self.scale, max_prefix,
+                                        max_suffix, workspace=ws)
+        return call
 
     def run_step(self, k_step: int):
         return self.step(k_step)

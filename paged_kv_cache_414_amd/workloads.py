@@ -214,6 +214,105 @@ def long_context(seed: int = 5, poison: bool = True, num_seqs: int = 8) -> Decod
                              poison=poison)
 
 
+@dataclasses.dataclass
+class SharedPrefixBatch(DecodeBatch):
+    """A decode batch whose sequences come in groups sharing their leading blocks.
+
+    Group g is sequences [group_starts[g], group_starts[g + 1]); each of them shares
+    its first prefix_lens[s] tokens (whole blocks, the same physical ids) with the
+    rest of its group.  Sequences outside every group have prefix_lens 0."""
+
+    group_starts: np.ndarray = None  # int32 [G + 1]
+    prefix_lens: np.ndarray = None  # int32 [S]
+
+    @property
+    def num_groups(self) -> int:
+        return int(self.group_starts.size - 1)
+
+    @property
+    def max_prefix_len(self) -> int:
+        return int(self.prefix_lens.max()) if self.prefix_lens.size else 0
+
+    @property
+    def max_suffix_len(self) -> int:
+        if not self.context_lens.size:
+            return 0
+        return int((self.context_lens - self.prefix_lens).max())
+
+
+def make_shared_prefix_batch(name: str, *, seed: int, group_sizes, num_heads: int,
+                             head_dim: int, block_size: int, prefix_blocks_low: int,
+                             prefix_blocks_high: int, suffix_low: int, suffix_high: int,
+                             ungrouped: int = 0, dtype=np.float16, pool_slack: float = 1.1,
+                             scale: float | None = None,
+                             poison: bool = True) -> SharedPrefixBatch:
+    """Draw a grouped batch: ``ungrouped`` unshared sequences first, then one group per
+    entry of ``group_sizes``.  A group's prefix is U[prefix_blocks_low,
+    prefix_blocks_high] whole blocks, each sequence's own tokens after it are
+    U[suffix_low, suffix_high] (ungrouped sequences: that many tokens in all).  Block
+    ids are a seeded random permutation of the pool, dealt out in order: a group's
+    shared blocks once, then every member's own blocks."""
+    dtype = np.dtype(dtype)
+    rng = np.random.default_rng(seed)
+    group_sizes = [int(n) for n in group_sizes]
+    prefix_blocks = rng.integers(prefix_blocks_low, prefix_blocks_high + 1,
+                                 size=len(group_sizes)).astype(np.int64)
+    num_seqs = int(ungrouped) + sum(group_sizes)
+    suffix = rng.integers(suffix_low, suffix_high + 1, size=num_seqs).astype(np.int64)
+    prefix_lens = np.zeros(num_seqs, dtype=np.int64)
+    starts = [int(ungrouped)]
+    for g, n in enumerate(group_sizes):
+        prefix_lens[starts[-1]:starts[-1] + n] = prefix_blocks[g] * block_size
+        starts.append(starts[-1] + n)
+    ctx = (prefix_lens + suffix).astype(np.int32)
+    own_blocks = [-(-int(c) // block_size) - int(p) // block_size
+                  for c, p in zip(ctx, prefix_lens)]
+    needed = int(prefix_blocks.sum()) + sum(own_blocks)
+    num_blocks = max(int(math.ceil(pool_slack * needed)), needed + 1)
+    max_blocks = max(1, max(-(-int(c) // block_size) for c in ctx) if num_seqs else 1)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    pad_id = int(perm[needed])  # an unused block: poisoned, never live
+    tables = np.full((num_seqs, max_blocks), pad_id, dtype=np.int32)
+    cursor = 0
+    for s in range(int(ungrouped)):
+        tables[s, :own_blocks[s]] = perm[cursor:cursor + own_blocks[s]]
+        cursor += own_blocks[s]
+    for g, n in enumerate(group_sizes):
+        shared = perm[cursor:cursor + int(prefix_blocks[g])]
+        cursor += int(prefix_blocks[g])
+        for s in range(starts[g], starts[g + 1]):
+            tables[s, :shared.size] = shared
+            tables[s, shared.size:shared.size + own_blocks[s]] = perm[cursor:cursor + own_blocks[s]]
+            cursor += own_blocks[s]
+    q = normal(rng, (num_seqs, num_heads, head_dim), dtype)
+    k_pool = normal(rng, (num_blocks, num_heads, block_size, head_dim), dtype)
+    v_pool = normal(rng, (num_blocks, num_heads, block_size, head_dim), dtype)
+    if poison:
+        live = _live_mask(tables, ctx, block_size, num_blocks)
+        poison_pool(k_pool, live)
+        poison_pool(v_pool, live)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return SharedPrefixBatch(name=name, dtype=dtype, num_heads=num_heads, head_dim=head_dim,
+                             block_size=block_size, num_blocks=num_blocks,
+                             max_blocks_per_seq=max_blocks, q=q, k_pool=k_pool,
+                             v_pool=v_pool, block_tables=tables, context_lens=ctx,
+                             scale=float(scale),
+                             group_starts=np.asarray(starts, dtype=np.int32),
+                             prefix_lens=prefix_lens.astype(np.int32))
+
+
+def shared_prefix_decode(seed: int = 4, poison: bool = True) -> SharedPrefixBatch:
+    """The shared-prefix mix at its last step as one batch: 8 groups x 8 samples x 32
+    heads x 128, block 16, fp16; every group shares a 1024-token prefix (64 blocks)
+    and each sample holds 257-271 tokens of its own (1-15 prompt tokens past the
+    prefix plus 256 generated ones)."""
+    return make_shared_prefix_batch("shared_prefix_decode", seed=seed, group_sizes=[8] * 8,
+                                    num_heads=32, head_dim=128, block_size=16,
+                                    prefix_blocks_low=64, prefix_blocks_high=64,
+                                    suffix_low=257, suffix_high=271, poison=poison)
+
+
 # ----------------------------------------------------------------------------------
 # dynamic step mixes: random decisions and values only; block bookkeeping is done
 # by the host allocator

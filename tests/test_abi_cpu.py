@@ -115,3 +115,56 @@ def test_append_and_copy_reject_bad_arguments(ops):
     assert lib.pa_block_copy(p, p, p, 2, 4, 96, 16, 64, 0, None) == 3
     assert lib.pa_block_copy(p, None, p, 2, 4, 64, 16, 64, 0, None) == 1
     assert lib.pa_block_copy(None, None, None, 0, 4, 64, 16, 64, 0, None) == 0
+
+
+def _bad_shared(ops, **over):
+    p = 1 << 20
+    args = dict(out=p, q=p, k=p, v=p, bt=p, ctx=p, gs=p, pl=p, S=16, H=4, D=128, bs=16, NB=64,
+                MB=8, G=2, maxp=64, maxs=64, scale=0.125, dtype=1, P=0, Pp=0, ws=p,
+                wsb=1 << 30)
+    args.update(over)
+    return ops.lib.pa_decode_shared_prefix(
+        args["out"], args["q"], args["k"], args["v"], args["bt"], args["ctx"], args["gs"],
+        args["pl"], args["S"], args["H"], args["D"], args["bs"], args["NB"], args["MB"],
+        args["G"], args["maxp"], args["maxs"], args["scale"], args["dtype"], args["P"],
+        args["Pp"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=0), 3),            # fp32 is not built for the shared-prefix decode
+    (dict(bs=8), 3),
+    (dict(D=96), 3),
+    (dict(maxp=40), 2),            # not a whole number of blocks
+    (dict(maxp=-16), 2),
+    (dict(maxs=-1), 2),
+    (dict(maxp=144), 2),           # more than max_blocks_per_seq * block_size
+    (dict(maxs=129), 2),
+    (dict(Pp=24), 2),              # prefix partitions are whole 16-token tiles
+    (dict(P=24), 2),
+    (dict(G=-1), 2),
+    (dict(scale=float("inf")), 2),
+    (dict(pl=None), 1),
+    (dict(gs=None), 1),
+    (dict(ws=None), 4),
+    (dict(wsb=16), 4),
+])
+def test_shared_prefix_rejects_bad_arguments(ops, over, status):
+    assert _bad_shared(ops, **over) == status
+    assert ops.lib.pa_last_error() != b""
+
+
+def test_shared_prefix_planning(ops):
+    # an empty batch needs nothing and enqueues nothing
+    assert _bad_shared(ops, S=0, out=None, q=None, k=None, v=None, bt=None, ctx=None,
+                       gs=None, pl=None, ws=None, wsb=0) == 0
+    s, h, d = 64, 32, 128
+    n = ops.pa_decode_shared_prefix_workspace_bytes(s, h, d, 16, 8, 1024, 272, 0, 256)
+    # 4 prefix partitions of 256 tokens + 1 partition for the 272 tokens after them
+    slots = 4 + ops.pa_decode_num_partitions(s, h, 16, 272, 0)
+    ml = -(-(s * h * slots * 4) // 256) * 256
+    assert n == 2 * ml + s * h * slots * d * 4
+    # a prefix that is not a whole number of blocks is refused
+    assert ops.lib.pa_decode_shared_prefix_workspace_bytes(s, h, d, 16, 8, 1000, 272, 0, 0) == 0
+    assert ops.lib.pa_last_error() != b""
+    with pytest.raises(ops.PagedAttentionError):
+        ops.pa_decode_shared_prefix_workspace_bytes(s, h, d, 16, 8, 1000, 272)

@@ -88,3 +88,16 @@ def test_shared_prefix_copy_on_write():
     rc = mix.manager.alloc.ref_count
     shared_full = [b for b in mix.manager.seqs[0].blocks[:64]]
     assert np.all(rc[shared_full] == 8)
+
+
+def test_shared_prefix_mix_with_shared_decode():
+    """The same mix with the decode run by pa_decode_shared_prefix: the 64 full prompt
+    blocks of each group are read once for its 8 samples."""
+    from paged_kv_cache_414_amd import steps
+    mix = steps.SharedPrefix(seed=4, keep_records=True, shared_decode=True)
+    last = mix.steps - 1
+    worst = replay(mix, decode_steps={0, 1, 2, 15, 100, last}, pool_steps={last})
+    print(f"shared prefix, shared decode: worst max-abs err {worst:.3e}")
+    rec = mix.records[-1]
+    starts, prefix = mix.shared_prefix(rec.block_tables, rec.context_lens)
+    assert np.all(prefix == 1024)

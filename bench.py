@@ -35,10 +35,10 @@ METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 # raw values are in profiles/decode_partitions_llama7b_pmc.md.  Valid only for the
 # kernel source they were taken on.
 MEASURED_TRAFFIC = {
-    "kernel_source_sha256": "84d0f19d381bd32c881f30d65736f473380c86306f3ac07e538bcafe32f7a7ad",
+    "kernel_source_sha256": "eefe3e232ae75da6bf2cf674581b52dd0a016346812f4dac6dde16cff4ffe02b",
     "seed": 2,
     "partition_tokens": 2048,
-    "read_bytes": 1934578720,
+    "read_bytes": 1934729055,
     "write_bytes": 786432,
 }
 KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -69,6 +69,8 @@ def parse():
                     help="time budget of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--no-mixes", dest="mixes", action="store_false",
                     help="skip the continuous-batching and shared-prefix step mixes")
+    ap.add_argument("--no-extras", dest="extras", action="store_false",
+                    help="skip the long-context and shared-prefix batches")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one pa_block_copy of a known size (counter calibration)")
     ap.add_argument("--quiet", action="store_true")
@@ -134,14 +136,14 @@ def cpu_baseline(batch, budget_s):
     }
 
 
-def run_mix(cls_name, seed, torch, args):
+def run_mix(cls_name, seed, torch, args, **kw):
     """One full run of a step mix: wall-clock seq-steps/s (host block manager, the
     small per-step H2D copies and the launches included; synthetic inputs staged in
     HBM beforehand) and the last step's decode re-timed alone."""
     from paged_kv_cache_414_amd import metrics, steps
 
-    log(args, f"step mix {cls_name}")
-    mix = getattr(steps, cls_name)(seed=seed)
+    log(args, f"step mix {cls_name} {kw}")
+    mix = getattr(steps, cls_name)(seed=seed, **kw)
     mix.prepare()  # every step's synthetic inputs drawn and placed in HBM
     t0 = time.perf_counter()
     rows = 0
@@ -161,6 +163,93 @@ def run_mix(cls_name, seed, torch, args):
         "last_step_decode_kv_gbps": round(metrics.gbps(kv, ms * 1e-3), 1),
         "last_step_sum_context": int(ctx.sum()),
         "note": "decode GB/s at this size may include Infinity Cache hits (working set < 256 MB)",
+    }
+
+
+def long_context_decode(torch, ops, metrics, args):
+    """pa_decode on the long-context batch (8 seqs x 32 heads x 128, block 32,
+    contexts U[16384, 32768]): partition pass + log-sum-exp merge."""
+    from paged_kv_cache_414_amd import workloads
+
+    log(args, "long-context batch")
+    b = workloads.long_context(seed=5, poison=False)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    q, k, v = dev(b.q), dev(b.k_pool), dev(b.v_pool)
+    tables, ctx = dev(b.block_tables), dev(b.context_lens)
+    out = torch.empty_like(q)
+    ws = ops.workspace_for(q, k, b.max_context_len, 0)
+
+    def decode():
+        ops.pa_decode(out, q, k, v, tables, ctx, b.scale, b.max_context_len, 0, ws)
+
+    def partitions():
+        ops.pa_decode_partitions(out, q, k, v, tables, ctx, b.scale, b.max_context_len, 0, ws)
+
+    for _ in range(5):
+        decode()
+    n = max(10, args.steps // 4)
+    ms = time_launches(decode, n, torch)
+    ms_part = time_launches(partitions, n, torch)
+    kv = metrics.decode_kv_bytes(b.context_lens, b.num_heads, b.head_dim, 2)
+    del q, k, v, tables, ctx, out, ws
+    torch.cuda.empty_cache()
+    return {
+        "sum_context": int(b.context_lens.sum()),
+        "partition_tokens": ops.pa_decode_partition_size(b.num_seqs, b.num_heads, b.block_size,
+                                                         b.max_context_len),
+        "num_partitions": ops.pa_decode_num_partitions(b.num_seqs, b.num_heads, b.block_size,
+                                                       b.max_context_len),
+        "decode_ms": round(ms, 5),
+        "decode_kv_gbps": round(metrics.gbps(kv, ms * 1e-3), 1),
+        "pct_of_hbm_peak": round(100.0 * metrics.gbps(kv, ms * 1e-3) / metrics.HBM_PEAK_GBPS, 2),
+        "partition_pass_ms": round(ms_part, 5),
+        "seq_steps_per_s": round(b.num_seqs / (ms * 1e-3), 1),
+    }
+
+
+def shared_prefix_decode(torch, ops, metrics, args):
+    """pa_decode against pa_decode_shared_prefix on the shared-prefix mix's last step
+    as one batch (8 groups x 8 samples sharing 1024 prompt tokens, 257-271 own tokens
+    each): logical bytes count every sequence's tokens, unique bytes count a shared
+    block once."""
+    from paged_kv_cache_414_amd import workloads
+
+    log(args, "shared-prefix batch")
+    b = workloads.shared_prefix_decode(seed=4, poison=False)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    q, k, v = dev(b.q), dev(b.k_pool), dev(b.v_pool)
+    tables, ctx = dev(b.block_tables), dev(b.context_lens)
+    starts, prefix = dev(b.group_starts), dev(b.prefix_lens)
+    out = torch.empty_like(q)
+    ws = ops.workspace_for(q, k, b.max_context_len, 0)
+    ws2 = ops.shared_prefix_workspace_for(q, k, b.num_groups, b.max_prefix_len, b.max_suffix_len)
+
+    def plain():
+        ops.pa_decode(out, q, k, v, tables, ctx, b.scale, b.max_context_len, 0, ws)
+
+    def shared():
+        ops.pa_decode_shared_prefix(out, q, k, v, tables, ctx, starts, prefix, b.scale,
+                                    b.max_prefix_len, b.max_suffix_len, workspace=ws2)
+
+    for _ in range(10):
+        plain()
+        shared()
+    n = max(20, args.steps)
+    ms_plain = time_launches(plain, n, torch)
+    ms_shared = time_launches(shared, n, torch)
+    per_token = metrics.kv_bytes_per_token(1, b.num_heads, b.head_dim, 2)
+    logical = metrics.decode_kv_bytes(b.context_lens, b.num_heads, b.head_dim, 2)
+    first = b.group_starts[:-1]
+    unique = per_token * int((b.context_lens - b.prefix_lens).sum() + b.prefix_lens[first].sum())
+    return {
+        "groups": b.num_groups, "seqs": b.num_seqs, "prefix_tokens": b.max_prefix_len,
+        "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+        "pa_decode_ms": round(ms_plain, 5),
+        "pa_decode_shared_prefix_ms": round(ms_shared, 5),
+        "speedup": round(ms_plain / ms_shared, 3),
+        "shared_unique_kv_gbps": round(metrics.gbps(unique, ms_shared * 1e-3), 1),
+        "shared_logical_kv_gbps": round(metrics.gbps(logical, ms_shared * 1e-3), 1),
+        "note": "pa_decode re-reads each shared block per sample (partly from cache)",
     }
 
 
@@ -283,10 +372,16 @@ def main():
             "algorithmic_bytes_per_launch": kv,
         },
     }
+    if args.extras:
+        record["long_context"] = long_context_decode(torch, ops, metrics, args)
+        record["shared_prefix_decode"] = shared_prefix_decode(torch, ops, metrics, args)
     if args.mixes:
-        record["step_mixes"] = {name: run_mix(cls, seed, torch, args)
-                                for name, cls, seed in (("continuous_batching", "ContinuousBatching", 3),
-                                                        ("shared_prefix_cow", "SharedPrefix", 4))}
+        record["step_mixes"] = {
+            "continuous_batching": run_mix("ContinuousBatching", 3, torch, args),
+            "shared_prefix_cow": run_mix("SharedPrefix", 4, torch, args),
+            "shared_prefix_cow_shared_decode": run_mix("SharedPrefix", 4, torch, args,
+                                                       shared_decode=True),
+        }
     if args.copy_probe:
         record["copy_probe"] = copy_probe(torch, ops, metrics)
     if args.cpu_seconds > 0:

@@ -77,7 +77,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 2,   /* a size or value is out of range or inconsistent */
   PA_ERR_UNSUPPORTED = 3,   /* dtype, head_dim or block_size not built */
   PA_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required */
-  PA_ERR_HIP = 5            /* the HIP runtime reported an error */
+  PA_ERR_HIP = 5,           /* the HIP runtime reported an error */
+  PA_ERR_OUT_OF_BLOCKS = 6  /* the block manager has too few free blocks (pa_blocks.h) */
 } pa_status;
 
 /* Version of this ABI (PA_ABI_VERSION of the library that was built). */

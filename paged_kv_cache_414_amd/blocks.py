@@ -1,5 +1,5 @@
-"""Host-side bookkeeping of the paged KV cache: free list, reference counts, block
-tables, slot mapping and the copy-on-write trigger.
+"""Host-side bookkeeping of the paged KV cache: the native block manager of
+``libpa.so`` (include/pa_blocks.h) under a small Python class, plus two helpers.
 
 Pages cited (title, then section):
   [Reading vLLM] "啃透vLLM源码：从PagedAttention到连续批处理，大模型推理加速24倍的秘密"
@@ -13,8 +13,8 @@ Pages cited (title, then section):
 * Physical blocks carry a reference count so that sequences can share them, e.g. a
   common prompt prefix ([Reading vLLM] §2.2, PhysicalTokenBlock.ref_count).
 * A sharer that must write into a shared block first gets its own copy
-  (copy-on-write, [vLLM basics] §2.3).  Here the first ref_count - 1 writers copy
-  and the last remaining holder writes in place.
+  (copy-on-write, [vLLM basics] §2.3).  The first ref_count - 1 writers copy and the
+  last remaining holder writes in place.
 * Admission follows the scheduler sketch of [Reading vLLM] §3: admit while blocks
   can be allocated, stop at the first request that does not fit.
 
@@ -23,153 +23,146 @@ Slot of logical token ``pos`` of a sequence: table[pos // bs] * bs + pos % bs.
 
 from __future__ import annotations
 
-import dataclasses
-
 import numpy as np
+
+from . import ops
 
 
 class OutOfBlocks(RuntimeError):
     pass
 
 
-class BlockAllocator:
-    """Physical block ids with reference counts.  A new block is drawn uniformly at
-    random from the free list when an RNG is given, else the lowest free id."""
-
-    def __init__(self, num_blocks: int, rng: np.random.Generator | None = None):
-        self.num_blocks = int(num_blocks)
-        self.ref_count = np.zeros(self.num_blocks, dtype=np.int64)
-        self._free = list(range(self.num_blocks))
-        if rng is None:
-            self._free.reverse()  # pop() then yields the lowest id
-        self._rng = rng
-
-    @property
-    def num_free(self) -> int:
-        return len(self._free)
-
-    def can_allocate(self, n: int) -> bool:
-        return n <= len(self._free)
-
-    def allocate(self) -> int:
-        if not self._free:
-            raise OutOfBlocks("no free block")
-        if self._rng is None:
-            b = self._free.pop()
-        else:
-            i = int(self._rng.integers(len(self._free)))
-            self._free[i], self._free[-1] = self._free[-1], self._free[i]
-            b = self._free.pop()
-        self.ref_count[b] = 1
-        return b
-
-    def incref(self, b: int) -> None:
-        if self.ref_count[b] <= 0:
-            raise ValueError(f"block {b} is not allocated")
-        self.ref_count[b] += 1
-
-    def decref(self, b: int) -> None:
-        if self.ref_count[b] <= 0:
-            raise ValueError(f"block {b} is not allocated")
-        self.ref_count[b] -= 1
-        if self.ref_count[b] == 0:
-            self._free.append(int(b))
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
 
 
-@dataclasses.dataclass
-class Sequence:
-    seq_id: int
-    blocks: list
-    length: int = 0
+def _ids(seq_ids) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
 
 
 class BlockManager:
-    """Block tables of live sequences over one pool."""
+    """Block tables of live sequences over one pool of ``num_blocks`` blocks.
 
-    def __init__(self, num_blocks: int, block_size: int,
-                 rng: np.random.Generator | None = None):
+    seed None or 0: a new block is the most recently freed one (initially the lowest
+    id); otherwise new blocks are drawn uniformly from the free list (SplitMix64
+    seeded with ``seed``)."""
+
+    def __init__(self, num_blocks: int, block_size: int, seed: int | None = None):
+        self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
-        self.alloc = BlockAllocator(num_blocks, rng)
-        self.seqs: dict[int, Sequence] = {}
+        self._lib = ops.lib
+        self._h = self._lib.pa_bm_create(self.num_blocks, self.block_size, int(seed or 0))
+        if not self._h:
+            raise ValueError(self._lib.pa_last_error().decode())
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._lib.pa_bm_destroy(h)
+
+    def _check(self, status: int) -> None:
+        if status == 0:
+            return
+        msg = self._lib.pa_last_error().decode()
+        if status == 6:
+            raise OutOfBlocks(msg)
+        if status == 2:
+            raise ValueError(msg)
+        raise ops.PagedAttentionError(status, msg)
 
     # -- queries ---------------------------------------------------------------------
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free(self._h))
+
     def blocks_needed(self, num_tokens: int) -> int:
         return -(-int(num_tokens) // self.block_size)
 
     def can_allocate(self, num_tokens: int) -> bool:
-        return self.alloc.can_allocate(self.blocks_needed(num_tokens))
+        return bool(self._lib.pa_bm_can_allocate(self._h, int(num_tokens)))
 
-    def slot(self, seq_id: int, pos: int) -> int:
-        seq = self.seqs[seq_id]
-        return seq.blocks[pos // self.block_size] * self.block_size + pos % self.block_size
+    def ref_counts(self) -> np.ndarray:
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        self._check(self._lib.pa_bm_ref_counts(self._h, _ptr(out)))
+        return out
+
+    def blocks_of(self, seq_id: int) -> list:
+        n = int(self._lib.pa_bm_num_seq_blocks(self._h, int(seq_id)))
+        if n < 0:
+            raise ValueError(f"unknown sequence {seq_id}")
+        out = np.empty(max(n, 1), dtype=np.int32)
+        self._check(self._lib.pa_bm_seq_blocks(self._h, int(seq_id), _ptr(out), n))
+        return out[:n].tolist()
 
     def context_len(self, seq_id: int) -> int:
-        return self.seqs[seq_id].length
+        return int(self.context_lens([seq_id])[0])
+
+    def slot(self, seq_id: int, pos: int) -> int:
+        blocks = self.blocks_of(seq_id)
+        return blocks[pos // self.block_size] * self.block_size + pos % self.block_size
 
     # -- life cycle ----------------------------------------------------------------
-    def add_sequence(self, seq_id: int, num_tokens: int) -> np.ndarray:
-        """Admit a sequence holding ``num_tokens`` prompt tokens; returns their slots."""
-        if seq_id in self.seqs:
-            raise ValueError(f"sequence {seq_id} exists")
-        n_blk = self.blocks_needed(num_tokens)
-        if not self.alloc.can_allocate(n_blk):
-            raise OutOfBlocks(f"{n_blk} blocks needed, {self.alloc.num_free} free")
-        seq = Sequence(seq_id, [self.alloc.allocate() for _ in range(n_blk)], int(num_tokens))
-        self.seqs[seq_id] = seq
-        # token p sits in block p // bs at offset p % bs
-        per_block = np.asarray(seq.blocks, dtype=np.int64)[:, None] * self.block_size
-        slots = (per_block + np.arange(self.block_size)[None, :]).reshape(-1)
-        return slots[:num_tokens].astype(np.int32)
+    def add_sequence(self, seq_id: int, num_tokens: int, slots: np.ndarray | None = None) -> np.ndarray:
+        """Admit a sequence holding ``num_tokens`` prompt tokens; returns their slots
+        (written into ``slots`` when given, an int32 array of at least that length)."""
+        n = int(num_tokens)
+        out = np.empty(max(n, 1), dtype=np.int32) if slots is None else slots
+        self._check(self._lib.pa_bm_add_sequence(self._h, int(seq_id), n, _ptr(out)))
+        return out[:n]
 
     def fork(self, parent_id: int, child_id: int) -> None:
         """The child shares every block of the parent (reference counts + 1)."""
-        if child_id in self.seqs:
-            raise ValueError(f"sequence {child_id} exists")
-        parent = self.seqs[parent_id]
-        for b in parent.blocks:
-            self.alloc.incref(b)
-        self.seqs[child_id] = Sequence(child_id, list(parent.blocks), parent.length)
-
-    def append_slot(self, seq_id: int):
-        """Reserve the slot of the sequence's next token.
-
-        Returns (slot, copy) where copy is None or (src, dst): the block that has to be
-        duplicated before the token is written, because the sequence shared it."""
-        seq = self.seqs[seq_id]
-        pos = seq.length
-        copy = None
-        if pos % self.block_size == 0:
-            if pos // self.block_size != len(seq.blocks):
-                raise AssertionError("table out of step with length")
-            seq.blocks.append(self.alloc.allocate())
-        else:
-            last = seq.blocks[-1]
-            if self.alloc.ref_count[last] > 1:
-                new = self.alloc.allocate()
-                self.alloc.decref(last)
-                seq.blocks[-1] = new
-                copy = (int(last), int(new))
-        seq.length = pos + 1
-        return self.slot(seq_id, pos), copy
+        self._check(self._lib.pa_bm_fork(self._h, int(parent_id), int(child_id)))
 
     def free(self, seq_id: int) -> None:
         """The sequence finished: every block it holds loses one reference."""
-        seq = self.seqs.pop(seq_id)
-        for b in seq.blocks:
-            self.alloc.decref(b)
+        self._check(self._lib.pa_bm_free(self._h, int(seq_id)))
+
+    def append_slots(self, seq_ids, slots=None, positions=None, pairs=None):
+        """Reserve the next token's slot of each listed sequence (all or nothing).
+
+        Returns (slots int32 [n], positions int32 [n], copy pairs int32 [c, 2]); the
+        pairs are blocks to duplicate (source, destination) before the tokens are
+        written.  Output arrays may be passed in (e.g. views of a staging buffer)."""
+        ids = _ids(seq_ids)
+        n = ids.size
+        slots = np.empty(max(n, 1), dtype=np.int32) if slots is None else slots
+        positions = np.empty(max(n, 1), dtype=np.int32) if positions is None else positions
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32) if pairs is None else pairs
+        count = np.zeros(1, dtype=np.int32)
+        self._check(self._lib.pa_bm_append_slots(self._h, _ptr(ids), n, _ptr(slots),
+                                                 _ptr(positions), _ptr(pairs), _ptr(count)))
+        return slots[:n], positions[:n], pairs[:int(count[0])]
+
+    def append_slot(self, seq_id: int):
+        """(slot, copy) for one sequence; copy is None or (src, dst)."""
+        slots, _, pairs = self.append_slots([seq_id])
+        copy = (int(pairs[0, 0]), int(pairs[0, 1])) if len(pairs) else None
+        return int(slots[0]), copy
 
     # -- device arrays -------------------------------------------------------------
-    def block_tables(self, seq_ids, max_blocks: int, pad: int = 0) -> np.ndarray:
-        out = np.full((len(seq_ids), max_blocks), pad, dtype=np.int32)
-        for i, sid in enumerate(seq_ids):
-            blocks = self.seqs[sid].blocks
-            if len(blocks) > max_blocks:
-                raise ValueError(f"sequence {sid} holds {len(blocks)} > {max_blocks} blocks")
-            out[i, :len(blocks)] = blocks
+    def block_tables(self, seq_ids, max_blocks: int, pad: int = 0,
+                     out: np.ndarray | None = None) -> np.ndarray:
+        ids = _ids(seq_ids)
+        out = np.empty((ids.size, int(max_blocks)), dtype=np.int32) if out is None else out
+        self._check(self._lib.pa_bm_block_tables(self._h, _ptr(ids), ids.size, int(max_blocks),
+                                                 int(pad), _ptr(out)))
         return out
 
-    def context_lens(self, seq_ids) -> np.ndarray:
-        return np.array([self.seqs[s].length for s in seq_ids], dtype=np.int32)
+    def context_lens(self, seq_ids, out: np.ndarray | None = None) -> np.ndarray:
+        ids = _ids(seq_ids)
+        out = np.empty(max(ids.size, 1), dtype=np.int32) if out is None else out
+        self._check(self._lib.pa_bm_context_lens(self._h, _ptr(ids), ids.size, _ptr(out)))
+        return out[:ids.size]
+
+    def shared_prefix_blocks(self, seq_ids) -> int:
+        """Leading whole blocks that every listed sequence holds as the same physical
+        blocks."""
+        ids = _ids(seq_ids)
+        n = int(self._lib.pa_bm_shared_prefix_blocks(self._h, _ptr(ids), ids.size))
+        if n < 0:
+            raise ValueError(self._lib.pa_last_error().decode())
+        return n
 
 
 def slots_for_positions(block_tables: np.ndarray, positions: np.ndarray,

@@ -13,12 +13,15 @@
 #include <cstdio>
 
 #include "pa_launch.h"
+#include "pa_status.h"
 
 namespace {
-
 thread_local char g_last_error[512] = "";
+}  // namespace
 
-pa_status fail(pa_status st, const char* fmt, ...) {
+namespace pa {
+
+pa_status set_error(pa_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
@@ -26,10 +29,18 @@ pa_status fail(pa_status st, const char* fmt, ...) {
   return st;
 }
 
-pa_status ok() {
+pa_status clear_error() {
   g_last_error[0] = '\0';
   return PA_OK;
 }
+
+}  // namespace pa
+
+namespace {
+
+using fail_fn = pa_status (*)(pa_status, const char*, ...);
+constexpr fail_fn fail = pa::set_error;
+pa_status ok() { return pa::clear_error(); }
 
 pa_status from_hip(hipError_t err, const char* what) {
   if (err == hipSuccess) return ok();
@@ -258,6 +269,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_OUT_OF_BLOCKS: return "PA_ERR_OUT_OF_BLOCKS";
   }
   return "PA_ERR_UNKNOWN";
 }

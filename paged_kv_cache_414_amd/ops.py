@@ -20,7 +20,7 @@ PA_F32 = 0
 PA_F16 = 1
 _DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16}
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_INVALID_ARG", 3: "PA_ERR_UNSUPPORTED",
-           4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP"}
+           4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP", 6: "PA_ERR_OUT_OF_BLOCKS"}
 
 # name -> (restype, argtypes), mirroring include/pa.h
 _i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
@@ -41,6 +41,21 @@ SIGNATURES = {
                                _vp]),
     "pa_block_copy": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32] * 9),
+    # host block manager (include/pa_blocks.h)
+    "pa_bm_create": (_vp, [_i32, _i32, ctypes.c_uint64]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_num_free": (_i32, [_vp]),
+    "pa_bm_can_allocate": (_i32, [_vp, _i32]),
+    "pa_bm_ref_counts": (_i32, [_vp, _vp]),
+    "pa_bm_add_sequence": (_i32, [_vp, ctypes.c_int64, _i32, _vp]),
+    "pa_bm_fork": (_i32, [_vp, ctypes.c_int64, ctypes.c_int64]),
+    "pa_bm_free": (_i32, [_vp, ctypes.c_int64]),
+    "pa_bm_append_slots": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "pa_bm_block_tables": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
+    "pa_bm_context_lens": (_i32, [_vp, _vp, _i32, _vp]),
+    "pa_bm_shared_prefix_blocks": (_i32, [_vp, _vp, _i32]),
+    "pa_bm_num_seq_blocks": (_i32, [_vp, ctypes.c_int64]),
+    "pa_bm_seq_blocks": (_i32, [_vp, ctypes.c_int64, _vp, _i32]),
     "pa_decode_shared_prefix": (_i32, [_vp] * 8 + [_i32] * 9 + [_f32, _i32, _i32, _i32, _vp,
                                                                 _sz, _vp]),
 }

@@ -1,4 +1,4 @@
-"""Step drivers: the host block manager steering the three device entry points.
+"""Step drivers: the host block manager steering the device entry points.
 
 Each step follows the request life cycle of "vLLM基础：架构、推理流程与关键组件"
 (vLLM basics) §2.2: slots for the new tokens are reserved first (a fresh block
@@ -7,12 +7,16 @@ new K/V rows are written, then attention runs with every context length counting
 the token just written; finished sequences give their blocks back and new ones are
 admitted (continuous batching, same page §2.4).
 
-On the device a step is: pa_block_copy (only when copy-on-write pairs are due),
-pa_cache_append of the step's rows, pa_decode, all on the current stream.  After
+Host side of a step (native block manager, include/pa_blocks.h): reserve the slots
+of every running sequence, build the block tables and context lengths, and for a
+continuous-batching step retire the finished sequences and admit new ones.  Every
+small array the device needs is written straight into one pinned staging buffer
+(two, used in turn) and moved with one asynchronous copy.  Device side, all on the
+current stream: pa_block_copy (only when copy-on-write pairs are due),
+pa_cache_append of the step's rows, the decode (pa_decode, or
+pa_decode_shared_prefix), then pa_cache_append of admitted prompts.  After
 :meth:`StepMix.prepare`, every step's synthetic inputs (new K/V rows, queries,
-prompts of admitted sequences) already sit in HBM, so that a step moves only its
-slot mapping, block tables, context lengths and copy pairs from the host (small
-copies through torch from pageable memory).
+prompts) already sit in HBM.
 
 Two step mixes are provided:
   * ContinuousBatching: 64 running sequences; after each step 13 of them finish and
@@ -66,18 +70,65 @@ class StepInputs:
     dev: tuple | None = None  # (new_k, new_v, q, prompt_k, prompt_v) on the device
 
 
+class Staging:
+    """Small int32 arrays of one step, written on the host into a pinned buffer and
+    moved to the device with one asynchronous copy.  Two pinned buffers are used in
+    turn; before one is rewritten, the copy that last read it has completed.  The
+    device buffer is reused every step: stream order puts the next copy after every
+    kernel that reads the previous step's arrays."""
+
+    ALIGN = 4  # int32 elements (16 bytes)
+
+    def __init__(self, capacity: int, device):
+        self.capacity = int(capacity)
+        self.host = [torch.empty(self.capacity, dtype=torch.int32, pin_memory=True)
+                     for _ in range(2)]
+        self.host_np = [h.numpy() for h in self.host]
+        self.events = [None, None]
+        self.dev = torch.empty(self.capacity, dtype=torch.int32, device=device)
+        self.turn = 0
+        self.used = 0
+
+    def begin(self) -> None:
+        ev = self.events[self.turn]
+        if ev is not None:
+            ev.synchronize()
+        self.used = 0
+
+    def take(self, n: int):
+        """(host view [n], offset) of the next n elements of this step."""
+        off = self.used
+        self.used += -(-int(n) // self.ALIGN) * self.ALIGN
+        if self.used > self.capacity:
+            raise RuntimeError(f"staging buffer too small ({self.used} > {self.capacity})")
+        return self.host_np[self.turn][off:off + int(n)], off
+
+    def device(self, off: int, shape) -> torch.Tensor:
+        n = int(np.prod(shape))
+        return self.dev[off:off + n].view(*shape)
+
+    def commit(self) -> None:
+        n = self.used
+        if n:
+            self.dev[:n].copy_(self.host[self.turn][:n], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record()
+            self.events[self.turn] = ev
+        self.turn ^= 1
+
+
 class StepMix:
     """Common driver: subclasses set up sequences and decide who finishes."""
 
     def __init__(self, spec: workloads.StepMixSpec, draws: workloads.StepDraws,
                  steps: int, max_blocks_per_seq: int, device="cuda",
-                 keep_records=False):
+                 keep_records=False, staging_extra: int = 0):
         self.spec = spec
         self.draws = draws
         self.steps = int(steps)
         self.mb = int(max_blocks_per_seq)
         self.manager = blocks.BlockManager(spec.num_blocks, spec.block_size,
-                                           draws.allocator_rng())
+                                           draws.allocator_seed())
         self.device = device
         torch_dtype = torch.float16 if spec.dtype == np.float16 else torch.float32
         shape = (spec.num_blocks, spec.num_heads, spec.block_size, spec.head_dim)
@@ -86,7 +137,7 @@ class StepMix:
         self.out = torch.empty((spec.num_seqs, spec.num_heads, spec.head_dim),
                                dtype=torch_dtype, device=device)
         self.ws = None
-        self.lanes: list[int] = []  # sequence id of each batch row
+        self.lanes = np.empty(0, dtype=np.int64)  # sequence id of each batch row
         self.records: list[StepRecord] = []
         self.keep = keep_records
         self.next_id = 0
@@ -95,6 +146,10 @@ class StepMix:
         self.scale = 1.0 / float(np.sqrt(spec.head_dim))
         self.last_decode = None
         self._inputs: dict[int, StepInputs] = {}
+        s = spec.num_seqs
+        per_step = 4 * s + s * self.mb + (s + 1) + s + 8 * Staging.ALIGN
+        self.staging = Staging(per_step + int(staging_extra), device)
+        self._positions = np.empty(s, dtype=np.int32)
 
     # -- inputs ---------------------------------------------------------------------
     def _draw_inputs(self, k: int) -> StepInputs:
@@ -121,9 +176,9 @@ class StepMix:
     def to_dev(self, a: np.ndarray) -> torch.Tensor:
         return torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
 
-    def _workspace(self, q, max_ctx):
-        need = ops.pa_decode_workspace_bytes(q.shape[0], q.shape[1], q.shape[2],
-                                             self.k_cache.shape[2], max_ctx, 0)
+    def _workspace(self, num_seqs, max_ctx):
+        need = ops.pa_decode_workspace_bytes(num_seqs, self.spec.num_heads, self.spec.head_dim,
+                                             self.spec.block_size, max_ctx, 0)
         if need and (self.ws is None or self.ws.numel() < need):
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self.ws if need else None
@@ -132,60 +187,78 @@ class StepMix:
         self.next_id += 1
         return self.next_id - 1
 
-    def _append_rows(self, slots, k, v, k_dev=None, v_dev=None):
-        if len(slots):
-            ops.pa_cache_append(self.k_cache, self.v_cache,
-                                self.to_dev(k) if k_dev is None else k_dev,
-                                self.to_dev(v) if v_dev is None else v_dev,
-                                self.to_dev(slots.astype(np.int32)))
-
-    def _admit_all(self, lens, k_rows, v_rows, k_dev=None, v_dev=None):
-        """Admit one sequence per entry of ``lens`` and write their prompt rows."""
-        ids, slots = [], []
+    def _admit(self, lens, slots_out: np.ndarray) -> list:
+        """Admit one sequence per entry of ``lens``; their prompt slots are written
+        into ``slots_out`` in admission order."""
+        ids, cursor = [], 0
         for n in lens:
+            n = int(n)
             sid = self._new_id()
-            slots.append(self.manager.add_sequence(sid, int(n)))
+            self.manager.add_sequence(sid, n, slots=slots_out[cursor:cursor + max(n, 1)])
+            cursor += n
             ids.append(sid)
-        slots = np.concatenate(slots)
-        self._append_rows(slots, k_rows, v_rows, k_dev, v_dev)
-        return ids, slots
+        return ids
+
+    def _write_rows(self, slots_d, k_rows, v_rows):
+        if slots_d.numel():
+            ops.pa_cache_append(self.k_cache, self.v_cache, k_rows, v_rows, slots_d)
 
     # -- one step -------------------------------------------------------------------
+    def _host_extra(self, k_step: int, st: Staging):
+        """Subclass hook, run after the decode arrays are staged and before the copy:
+        returns a callable that enqueues this step's work after the decode, or None."""
+        return None
+
     def step(self, k_step: int):
-        pairs, slots, positions = [], [], []
-        for sid in self.lanes:
-            pos = self.manager.context_len(sid)
-            slot, cow = self.manager.append_slot(sid)
-            if cow is not None:
-                pairs.append(cow)
-            slots.append(slot)
-            positions.append(pos)
-        pairs = np.array(pairs, dtype=np.int32).reshape(-1, 2)
-        slots = np.array(slots, dtype=np.int32)
-        tables = self.manager.block_tables(self.lanes, self.mb)
-        ctx = self.manager.context_lens(self.lanes)
+        st = self.staging
+        st.begin()
+        n = len(self.lanes)
+        slots_h, o_slots = st.take(n)
+        pairs_h, o_pairs = st.take(2 * n)
+        tables_h, o_tables = st.take(n * self.mb)
+        ctx_h, o_ctx = st.take(n)
+        slots, positions, pairs = self.manager.append_slots(
+            self.lanes, slots=slots_h, positions=self._positions, pairs=pairs_h.reshape(n, 2))
+        tables = self.manager.block_tables(self.lanes, self.mb, out=tables_h.reshape(n, self.mb))
+        ctx = self.manager.context_lens(self.lanes, out=ctx_h)
         max_ctx = int(ctx.max())
         self.copies_total += len(pairs)
-        inp = self.inputs(k_step)
-        nk_d, nv_d, q_d = inp.dev[:3] if inp.dev else (None, None, None)
-
-        if len(pairs):
-            ops.pa_block_copy(self.k_cache, self.v_cache, self.to_dev(pairs))
-        self._append_rows(slots, inp.new_k, inp.new_v, nk_d, nv_d)
-        q_d = self.to_dev(inp.q) if q_d is None else q_d
-        tables_d, ctx_d = self.to_dev(tables), self.to_dev(ctx)
-        self.last_decode = self._decode_call(q_d, tables, tables_d, ctx, ctx_d, max_ctx)
-        self.last_decode()
         if self.keep:
-            self.records.append(StepRecord(k_step, pairs, slots, inp.new_k, inp.new_v,
-                                           np.array(positions), tables, ctx, inp.q))
+            rec = StepRecord(k_step, pairs.copy(), slots.copy(), None, None, positions.copy(),
+                             tables.copy(), ctx.copy(), None)
+        decode = self._decode_call(k_step, st, tables, ctx, o_tables, o_ctx, max_ctx)
+        after = self._host_extra(k_step, st)
+        st.commit()
+
+        inp = self.inputs(k_step)
+        nk_d, nv_d, q_d = inp.dev[:3] if inp.dev else (self.to_dev(inp.new_k),
+                                                        self.to_dev(inp.new_v),
+                                                        self.to_dev(inp.q))
+        if len(pairs):
+            ops.pa_block_copy(self.k_cache, self.v_cache, st.device(o_pairs, (len(pairs), 2)))
+        self._write_rows(st.device(o_slots, (n,)), nk_d, nv_d)
+        self.last_decode = lambda: decode(q_d)
+        self.last_decode()
+        if after is not None:
+            after()
+        if self.keep:
+            rec.new_k, rec.new_v, rec.q = inp.new_k, inp.new_v, inp.q
+            self._finish_record(rec)
+            self.records.append(rec)
         return ctx
 
-    def _decode_call(self, q_d, tables, tables_d, ctx, ctx_d, max_ctx):
-        """The step's decode as a callable (enqueued once per step; again for timing)."""
-        ws = self._workspace(q_d, max_ctx)
+    def _finish_record(self, rec: StepRecord) -> None:
+        pass
 
-        def call():
+    def _decode_call(self, k_step, st, tables, ctx, o_tables, o_ctx, max_ctx):
+        """The step's decode as a callable of the query (enqueued once per step, and
+        again for timing)."""
+        n = len(self.lanes)
+        tables_d = st.device(o_tables, (n, self.mb))
+        ctx_d = st.device(o_ctx, (n,))
+        ws = self._workspace(n, max_ctx)
+
+        def call(q_d):
             ops.pa_decode(self.out, q_d, self.k_cache, self.v_cache, tables_d, ctx_d,
                           self.scale, max_ctx, 0, ws)
         return call
@@ -208,11 +281,17 @@ class ContinuousBatching(StepMix):
         draws = workloads.ContinuousBatchingDraws(spec, seed)
         steps = steps or spec.steps
         mb = -(-(draws.prompt_high + steps) // spec.block_size)
-        super().__init__(spec, draws, steps, mb, device, keep_records)
+        prompt_room = draws.finish_count * draws.prompt_high + Staging.ALIGN
+        super().__init__(spec, draws, steps, mb, device, keep_records, staging_extra=prompt_room)
         lens = draws.initial_prompt_lens()
         k, v = draws.prompt_kv(-1, lens)
-        self.lanes, slots = self._admit_all(lens, k, v)
+        slots = np.empty(int(lens.sum()) + 1, dtype=np.int32)
+        self.lanes = np.array(self._admit(lens, slots), dtype=np.int64)
+        slots = slots[:int(lens.sum())]
+        ops.pa_cache_append(self.k_cache, self.v_cache, self.to_dev(k), self.to_dev(v),
+                            self.to_dev(slots))
         self.initial = (slots, k, v)
+        self._post = None
 
     def _draw_inputs(self, k: int) -> StepInputs:
         inp = super()._draw_inputs(k)
@@ -220,21 +299,30 @@ class ContinuousBatching(StepMix):
         inp.prompt_k, inp.prompt_v = self.draws.prompt_kv(k, inp.prompt_lens)
         return inp
 
-    def run_step(self, k_step: int):
-        ctx = self.step(k_step)
-        # retire and admit; the new prompts are written before the next step
+    def _host_extra(self, k_step: int, st: Staging):
+        # retire and admit: the decode arrays are already staged, so the blocks of the
+        # finished sequences can be reused by the new prompts, which are written
+        # after the decode in stream order
         inp = self.inputs(k_step)
         finishing = self.draws.finishing(k_step)
         for lane in finishing:
-            self.manager.free(self.lanes[lane])
-        k_dev, v_dev = inp.dev[3:] if inp.dev else (None, None)
-        ids, slots = self._admit_all(inp.prompt_lens, inp.prompt_k, inp.prompt_v, k_dev, v_dev)
-        for lane, sid in zip(finishing, ids):
-            self.lanes[lane] = sid
-        if self.keep:
-            rec = self.records[-1]
-            rec.post_slots, rec.post_k, rec.post_v = slots, inp.prompt_k, inp.prompt_v
-        return ctx
+            self.manager.free(int(self.lanes[lane]))
+        total = int(inp.prompt_lens.sum())
+        pslots_h, o_p = st.take(total + 1)
+        ids = self._admit(inp.prompt_lens, pslots_h)
+        self.lanes[finishing] = ids
+        self._post = pslots_h[:total].copy() if self.keep else None
+        pslots_d = st.device(o_p, (total,))
+        k_dev, v_dev = inp.dev[3:] if inp.dev else (self.to_dev(inp.prompt_k),
+                                                     self.to_dev(inp.prompt_v))
+        return lambda: self._write_rows(pslots_d, k_dev, v_dev)
+
+    def _finish_record(self, rec: StepRecord) -> None:
+        inp = self.inputs(rec.step)
+        rec.post_slots, rec.post_k, rec.post_v = self._post, inp.prompt_k, inp.prompt_v
+
+    def run_step(self, k_step: int):
+        return self.step(k_step)
 
 
 class SharedPrefix(StepMix):
@@ -255,46 +343,56 @@ class SharedPrefix(StepMix):
         mb = -(-(int(lens.max()) + steps) // spec.block_size)
         super().__init__(spec, draws, steps, mb, device, keep_records)
         k, v = draws.prompt_kv(-1, lens)
-        leaders, slots = self._admit_all(lens, k, v)
+        slots = np.empty(int(lens.sum()) + 1, dtype=np.int32)
+        leaders = self._admit(lens, slots)
+        slots = slots[:int(lens.sum())]
+        lanes = []
         for leader in leaders:
-            group = [leader]
+            lanes.append(leader)
             for _ in range(draws.samples - 1):
                 child = self._new_id()
                 self.manager.fork(leader, child)
-                group.append(child)
-            self.lanes.extend(group)
+                lanes.append(child)
+        self.lanes = np.array(lanes, dtype=np.int64)
+        ops.pa_cache_append(self.k_cache, self.v_cache, self.to_dev(k), self.to_dev(v),
+                            self.to_dev(slots))
         self.initial = (slots, k, v)
 
-    def shared_prefix(self, tables: np.ndarray, ctx: np.ndarray):
-        """(group_starts, prefix_lens): the lanes of a group are contiguous; its
-        prefix is the leading whole blocks whose ids every member's table holds."""
+    def shared_prefix(self):
+        """(group_starts, prefix_lens) of the running lanes: a group is 8 contiguous
+        lanes; its prefix is the leading whole blocks all of its members hold."""
         n = self.draws.samples
         starts = np.arange(0, len(self.lanes) + 1, n, dtype=np.int32)
         prefix = np.zeros(len(self.lanes), dtype=np.int32)
-        bs = self.spec.block_size
         for r0 in starts[:-1]:
-            rows = tables[r0:r0 + n]
-            same = np.all(rows == rows[0], axis=0)
-            lead = int(np.argmin(same)) if not same.all() else same.size
-            lead = min(lead, int(ctx[r0:r0 + n].min()) // bs)
-            prefix[r0:r0 + n] = lead * bs
+            prefix[r0:r0 + n] = (self.manager.shared_prefix_blocks(self.lanes[r0:r0 + n]) *
+                                 self.spec.block_size)
         return starts, prefix
 
-    def _decode_call(self, q_d, tables, tables_d, ctx, ctx_d, max_ctx):
+    def _decode_call(self, k_step, st, tables, ctx, o_tables, o_ctx, max_ctx):
         if not self.shared_decode:
-            return super()._decode_call(q_d, tables, tables_d, ctx, ctx_d, max_ctx)
-        starts, prefix = self.shared_prefix(tables, ctx)
+            return super()._decode_call(k_step, st, tables, ctx, o_tables, o_ctx, max_ctx)
+        n = len(self.lanes)
+        starts, prefix = self.shared_prefix()
+        starts_h, o_starts = st.take(len(starts))
+        prefix_h, o_prefix = st.take(n)
+        starts_h[:] = starts
+        prefix_h[:] = prefix
+        self.last_prefix = (starts, prefix)
         max_prefix = int(prefix.max())
         max_suffix = int((ctx - prefix).max())
-        starts_d, prefix_d = self.to_dev(starts), self.to_dev(prefix)
+        tables_d = st.device(o_tables, (n, self.mb))
+        ctx_d = st.device(o_ctx, (n,))
+        starts_d = st.device(o_starts, (len(starts),))
+        prefix_d = st.device(o_prefix, (n,))
         need = ops.pa_decode_shared_prefix_workspace_bytes(
-            q_d.shape[0], q_d.shape[1], q_d.shape[2], self.spec.block_size, len(starts) - 1,
+            n, self.spec.num_heads, self.spec.head_dim, self.spec.block_size, len(starts) - 1,
             max_prefix, max_suffix)
         if self.ws_shared is None or self.ws_shared.numel() < need:
             self.ws_shared = torch.empty(need, dtype=torch.uint8, device=self.device)
         ws = self.ws_shared
 
-        def call():
+        def call(q_d):
             ops.pa_decode_shared_prefix(self.out, q_d, self.k_cache, self.v_cache, tables_d,
                                         ctx_d, starts_d, prefix_d, self.scale, max_prefix,
                                         max_suffix, workspace=ws)

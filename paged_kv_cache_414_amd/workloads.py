@@ -352,8 +352,9 @@ class StepDraws:
         # step -1 stands for draws made before the first step
         return np.random.default_rng([self.seed, int(step) + 1, int(stream)])
 
-    def allocator_rng(self) -> np.random.Generator:
-        return np.random.default_rng([self.seed, 1 << 20])
+    def allocator_seed(self) -> int:
+        """Non-zero seed of the block manager's random choice of free blocks."""
+        return int(np.random.default_rng([self.seed, 1 << 20]).integers(1, 1 << 62))
 
     def new_token_kv(self, step: int, n: int) -> tuple[np.ndarray, np.ndarray]:
         s = self.spec

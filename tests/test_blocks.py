@@ -1,5 +1,7 @@
-"""Host block manager: reference counts, copy-on-write, reclaim on finish, admission,
-and slot mapping checked against the oracle's own recomputation from the tables."""
+"""Host block manager (native, through the binding): reference counts, copy-on-write,
+reclaim on finish, admission, all-or-nothing appends, and slot mapping checked
+against the oracle's own recomputation from the tables, also over a long
+randomized run of admissions, forks, appends and frees."""
 
 from __future__ import annotations
 
@@ -19,11 +21,22 @@ def test_block_table_example_slots():
     assert slots.tolist() == [113, 159]
 
 
+def test_lowest_free_block_first_without_a_seed():
+    m = blocks.BlockManager(8, 16)
+    assert m.add_sequence(0, 20).tolist()[:2] == [0, 1]
+    assert m.blocks_of(0) == [0, 1]
+    m.add_sequence(1, 1)
+    assert m.blocks_of(1) == [2]
+    m.free(0)  # releases blocks 0, then 1
+    m.add_sequence(2, 1)  # the most recently freed block is reused first
+    assert m.blocks_of(2) == [1]
+
+
 def test_allocation_on_demand_and_random_draws():
-    m = blocks.BlockManager(64, 16, np.random.default_rng(0))
+    m = blocks.BlockManager(64, 16, seed=7)
     slots = m.add_sequence(0, 40)
-    assert len(m.seqs[0].blocks) == 3 and m.alloc.num_free == 61
-    assert len(set(m.seqs[0].blocks)) == 3
+    assert len(m.blocks_of(0)) == 3 and m.num_free == 61
+    assert len(set(m.blocks_of(0))) == 3
     # slots agree with the oracle's recomputation from the table
     t = m.block_tables([0], 4)
     assert slots.tolist() == oracle.slots_for_positions(t, [0] * 40, range(40), 16).tolist()
@@ -32,49 +45,81 @@ def test_allocation_on_demand_and_random_draws():
         slot, cow = m.append_slot(0)
         assert cow is None
         assert slot == oracle.slot_of(m.block_tables([0], 4)[0], pos, 16)
-    assert len(m.seqs[0].blocks) == 4
+    assert len(m.blocks_of(0)) == 4
+    # a different seed draws different blocks
+    other = blocks.BlockManager(64, 16, seed=8)
+    other.add_sequence(0, 40)
+    assert other.blocks_of(0) != m.blocks_of(0)[:3]
 
 
 def test_free_returns_every_block():
     m = blocks.BlockManager(32, 16)
     m.add_sequence(1, 100)
     m.add_sequence(2, 20)
-    assert m.alloc.num_free == 32 - 7 - 2
+    assert m.num_free == 32 - 7 - 2
     m.free(1)
-    assert m.alloc.num_free == 32 - 2
+    assert m.num_free == 32 - 2
     m.free(2)
-    assert m.alloc.num_free == 32 and np.all(m.alloc.ref_count == 0)
+    assert m.num_free == 32 and np.all(m.ref_counts() == 0)
 
 
 def test_fork_shares_and_copy_on_write():
     """8 samples share a 1030-token prompt: 64 full blocks + one block with 6 tokens.
     The first 7 writers copy the partial block; the last writes in place."""
-    m = blocks.BlockManager(256, 16, np.random.default_rng(1))
+    m = blocks.BlockManager(256, 16, seed=1)
     m.add_sequence(0, 1030)
     for c in range(1, 8):
         m.fork(0, c)
-    shared = list(m.seqs[0].blocks)
-    assert np.all(m.alloc.ref_count[shared] == 8)
-    copies = []
+    shared = m.blocks_of(0)
+    assert np.all(m.ref_counts()[shared] == 8)
+    assert m.shared_prefix_blocks(range(8)) == 64  # whole blocks only
+    slots, positions, pairs = m.append_slots(range(8))
+    assert positions.tolist() == [1030] * 8
     for sid in range(8):
-        slot, cow = m.append_slot(sid)
-        if cow is not None:
-            copies.append(cow)
-        assert slot == oracle.slot_of(m.seqs[sid].blocks, 1030, 16)
-    assert len(copies) == 7
-    assert all(src == shared[-1] for src, _ in copies)
-    assert len({dst for _, dst in copies}) == 7
-    assert m.seqs[7].blocks[-1] == shared[-1]  # the last holder kept the original
-    assert m.alloc.ref_count[shared[-1]] == 1
-    assert np.all(m.alloc.ref_count[shared[:-1]] == 8)  # full prefix blocks stay shared
+        assert slots[sid] == oracle.slot_of(m.blocks_of(sid), 1030, 16)
+    assert len(pairs) == 7
+    assert all(src == shared[-1] for src, _ in pairs)
+    assert len({dst for _, dst in pairs}) == 7
+    assert m.blocks_of(7)[-1] == shared[-1]  # the last holder kept the original
+    rc = m.ref_counts()
+    assert rc[shared[-1]] == 1
+    assert np.all(rc[shared[:-1]] == 8)  # full prefix blocks stay shared
+    assert m.shared_prefix_blocks(range(8)) == 64
     # the next token of each sample goes to its own partial block, no more copies
-    for sid in range(8):
-        _, cow = m.append_slot(sid)
-        assert cow is None
-    # finishing all samples frees everything
+    _, _, pairs = m.append_slots(range(8))
+    assert len(pairs) == 0
     for sid in range(8):
         m.free(sid)
-    assert m.alloc.num_free == 256
+    assert m.num_free == 256
+
+
+def test_repeated_ids_take_consecutive_tokens():
+    m = blocks.BlockManager(16, 4)
+    m.add_sequence(0, 2)
+    m.fork(0, 1)
+    slots, positions, pairs = m.append_slots([0, 0, 0, 1])
+    assert positions.tolist() == [2, 3, 4, 2]
+    assert len(pairs) == 1  # only the first write into the shared block copies
+    t = m.block_tables([0, 1], 4, pad=-1)
+    for (s, p), slot in zip([(0, 2), (0, 3), (0, 4), (1, 2)], slots):
+        assert slot == oracle.slot_of(t[s], p, 4)
+    assert m.context_lens([0, 1]).tolist() == [5, 3]
+
+
+def test_append_is_all_or_nothing():
+    m = blocks.BlockManager(4, 4)
+    m.add_sequence(0, 4)
+    m.add_sequence(1, 4)
+    m.add_sequence(2, 3)
+    m.fork(2, 3)  # 3 blocks used + one shared partial block; 1 free
+    # seq 0 and 1 need a new block each, seq 2 a copy: 3 > 1 free
+    before = (m.num_free, m.ref_counts().tolist(), m.context_lens([0, 1, 2, 3]).tolist())
+    with pytest.raises(blocks.OutOfBlocks):
+        m.append_slots([0, 1, 2])
+    assert (m.num_free, m.ref_counts().tolist(), m.context_lens([0, 1, 2, 3]).tolist()) == before
+    # both sharers of a block with 2 holders: one copy, one in place -> fits 1 free
+    _, _, pairs = m.append_slots([2, 3])
+    assert len(pairs) == 1 and m.num_free == 0
 
 
 def test_admission_fills_the_pool_exactly():
@@ -82,7 +127,7 @@ def test_admission_fills_the_pool_exactly():
     waiting = [(0, 64), (1, 64), (2, 16), (3, 16), (4, 1)]  # 4 + 4 + 1 + 1 blocks, then none
     admitted = blocks.admit_while_possible(m, waiting)
     assert admitted == [0, 1, 2, 3]
-    assert waiting == [(4, 1)] and m.alloc.num_free == 0
+    assert waiting == [(4, 1)] and m.num_free == 0
 
 
 def test_admission_breaks_on_misfit_even_if_later_fits():
@@ -100,13 +145,90 @@ def test_out_of_blocks_raises():
         m.append_slot(0)
     with pytest.raises(blocks.OutOfBlocks):
         m.add_sequence(1, 1)
+    assert m.context_len(0) == 32
 
 
-def test_refcount_errors():
-    a = blocks.BlockAllocator(4)
-    b = a.allocate()
-    a.decref(b)
+def test_bad_calls_raise():
     with pytest.raises(ValueError):
-        a.decref(b)
+        blocks.BlockManager(0, 16)
+    m = blocks.BlockManager(8, 16)
+    m.add_sequence(0, 5)
     with pytest.raises(ValueError):
-        a.incref(b)
+        m.add_sequence(0, 5)  # exists
+    with pytest.raises(ValueError):
+        m.fork(9, 10)  # unknown parent
+    with pytest.raises(ValueError):
+        m.fork(0, 0)  # child exists
+    with pytest.raises(ValueError):
+        m.free(3)
+    with pytest.raises(ValueError):
+        m.append_slots([0, 4])
+    with pytest.raises(ValueError):
+        m.block_tables([0], 0)
+    m.add_sequence(1, 40)
+    with pytest.raises(ValueError):
+        m.block_tables([1], 2)  # holds 3 blocks
+    with pytest.raises(ValueError):
+        m.shared_prefix_blocks([])
+
+
+def test_randomized_invariants():
+    """Random admissions, forks, appends (with copy-on-write) and frees.  After each
+    append every returned slot is the oracle's slot of that position in the updated
+    table, and every copy's destination is a fresh private block; after every
+    operation each block's reference count equals the number of tables holding it,
+    free + held blocks = pool, and context lengths match."""
+    rng = np.random.default_rng(5)
+    bs, nb = 8, 96
+    m = blocks.BlockManager(nb, bs, seed=3)
+    length = {}
+    next_id = 0
+    copies_seen = 0
+    for _ in range(600):
+        op = int(rng.integers(4))
+        if op == 0 or not length:
+            n = int(rng.integers(0, 40))
+            if m.can_allocate(n):
+                m.add_sequence(next_id, n)
+                length[next_id] = n
+            else:
+                with pytest.raises(blocks.OutOfBlocks):
+                    m.add_sequence(next_id, n)
+            next_id += 1
+        elif op == 1:
+            parent = int(rng.choice(list(length)))
+            m.fork(parent, next_id)
+            length[next_id] = length[parent]
+            next_id += 1
+        elif op == 2:
+            ids = [int(x) for x in rng.choice(list(length), size=int(rng.integers(1, 6)))]
+            try:
+                slots, positions, pairs = m.append_slots(ids)
+            except blocks.OutOfBlocks:
+                continue
+            rc = m.ref_counts()
+            for dst in pairs[:, 1]:
+                assert rc[dst] == 1
+            copies_seen += len(pairs)
+            for sid, slot, pos in zip(ids, slots, positions):
+                assert pos == length[sid]
+                length[sid] += 1
+                table = np.array(m.blocks_of(sid), dtype=np.int32)
+                assert slot == oracle.slot_of(table, int(pos), bs)
+        else:
+            sid = int(rng.choice(list(length)))
+            m.free(sid)
+            del length[sid]
+        rc = m.ref_counts()
+        holders = np.zeros(nb, dtype=np.int64)
+        for sid, n in length.items():
+            blk = m.blocks_of(sid)
+            assert len(blk) == -(-n // bs)
+            for b in blk:
+                holders[b] += 1
+        assert np.array_equal(rc, holders)
+        assert m.num_free + int(np.count_nonzero(holders)) == nb
+        if length:
+            ids = sorted(length)
+            assert m.context_lens(ids).tolist() == [length[s] for s in ids]
+    assert copies_seen > 0

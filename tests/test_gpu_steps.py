@@ -70,8 +70,9 @@ def test_continuous_batching_all_steps():
     worst = replay(mix, decode_steps=set(range(mix.steps)), pool_steps={0, 1, 25, mix.steps - 1})
     print(f"continuous batching: worst max-abs err {worst:.3e}")
     # 13 sequences were replaced after every step and every block is accounted for
-    live = sum(len(s.blocks) for s in mix.manager.seqs.values())
-    assert live + mix.manager.alloc.num_free == mix.spec.num_blocks
+    held = np.count_nonzero(mix.manager.ref_counts())
+    assert held + mix.manager.num_free == mix.spec.num_blocks
+    assert sum(len(mix.manager.blocks_of(int(s))) for s in mix.lanes) == held
     assert mix.copies_total == 0
 
 
@@ -85,8 +86,8 @@ def test_shared_prefix_copy_on_write():
     assert len(mix.records[0].copy_pairs) == 56
     assert all(len(r.copy_pairs) == 0 for r in mix.records[1:])
     # the 64 full prompt blocks of each group are still shared by its 8 samples
-    rc = mix.manager.alloc.ref_count
-    shared_full = [b for b in mix.manager.seqs[0].blocks[:64]]
+    rc = mix.manager.ref_counts()
+    shared_full = mix.manager.blocks_of(int(mix.lanes[0]))[:64]
     assert np.all(rc[shared_full] == 8)
 
 
@@ -98,6 +99,5 @@ def test_shared_prefix_mix_with_shared_decode():
     last = mix.steps - 1
     worst = replay(mix, decode_steps={0, 1, 2, 15, 100, last}, pool_steps={last})
     print(f"shared prefix, shared decode: worst max-abs err {worst:.3e}")
-    rec = mix.records[-1]
-    starts, prefix = mix.shared_prefix(rec.block_tables, rec.context_lens)
+    starts, prefix = mix.last_prefix
     assert np.all(prefix == 1024)

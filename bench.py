@@ -73,6 +73,8 @@ def parse():
                     help="skip the long-context and shared-prefix batches")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one pa_block_copy of a known size (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark: pa_decode by block size and head dim")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -284,6 +286,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.sweep:
+        from paged_kv_cache_414_amd import sweep
+        log(args, "block-size and head-dim sweep")
+        print(json.dumps(sweep.run(seed=args.seed, steps=min(args.steps, 50))), flush=True)
+        return
 
     log(args, "generating the llama7b_decode batch")
     batch = workloads.llama7b_decode(seed=args.seed, poison=False)

@@ -66,10 +66,11 @@ size_t ws_align(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 pa_status check_dtype_shape(pa_dtype dtype, int32_t head_dim, int32_t block_size) {
   if (dtype != PA_F32 && dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "dtype %d is not PA_F32 or PA_F16", (int)dtype);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 128)", head_dim);
-  if (block_size != 8 && block_size != 16 && block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not built (8, 16, 32)", block_size);
+  if (head_dim != 64 && head_dim != 80 && head_dim != 96 && head_dim != 128 && head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 80, 96, 128, 256)", head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128 &&
+      block_size != 256)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not built (8, 16, 32, 64, 128, 256)", block_size);
   return PA_OK;
 }
 
@@ -228,8 +229,8 @@ pa_status plan_shared(SharedPlan* plan, int32_t num_seqs, int32_t num_heads, int
                       int32_t prefix_partition_size) {
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 128)", head_dim);
-  if (block_size != 16 && block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not built for the shared-prefix decode (16, 32)",
+  if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128 && block_size != 256)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not built for the shared-prefix decode (16 to 256)",
                 block_size);
   if (num_seqs < 0 || num_heads <= 0 || num_groups < 0)
     return fail(PA_ERR_INVALID_ARG, "num_seqs %d >= 0, num_heads %d > 0, num_groups %d >= 0 required",

@@ -45,6 +45,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #ifndef PA_NONTEMPORAL_KV
 #define PA_NONTEMPORAL_KV 1  // 1: K/V loads carry the non-temporal (streaming) hint
 #endif
+#ifndef PA_MAX_LOADS_PER_UNIT
+#define PA_MAX_LOADS_PER_UNIT 8  // K (and V) loads per lane for one unit of a block
+#endif
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 0  // >0: cap registers so this many waves fit per SIMD
 #endif
@@ -155,18 +158,34 @@ template <> struct Lane16<float> {
   __device__ __forceinline__ static float from_float(float x) { return x; }
 };
 
-// Compile-time geometry of one (dtype, head_dim, block_size) instance.
+constexpr int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p *= 2;
+  return p;
+}
+
+// Compile-time geometry of one (dtype, head_dim, block_size) instance.  A token row
+// is spread over kLanesPerTok lanes (a power of two), of which the first kActive hold
+// 16 bytes of it; when D / kVec is not a power of two the other lanes of the row
+// are idle (their scores are masked to zero and their sums never leave the lane).
+// A unit is the run of consecutive tokens of one block that a wave folds at once:
+// the whole block, or a slice of it when the block would need more than
+// PA_MAX_LOADS_PER_UNIT loads.
 template <typename T, int D, int BS>
 struct Geometry {
   static constexpr int kVec = Lane16<T>::kVec;             // elements per 16-byte load
-  static constexpr int kLanesPerTok = D / kVec;            // lanes covering one token row
+  static constexpr int kActive = D / kVec;                 // lanes with data in a row
+  static constexpr int kLanesPerTok = pow2_ceil(kActive);  // lanes per token row
   static constexpr int kTokPerLoad = kWave / kLanesPerTok; // token rows per wave-wide load
-  static constexpr int kLoads = BS / kTokPerLoad;          // loads per (block, head) chunk
-  // blocks fetched together per wave: PA_KV_LOADS_IN_FLIGHT 16-byte loads per lane
+  static constexpr int kUnitTok =
+      BS < kTokPerLoad * PA_MAX_LOADS_PER_UNIT ? BS : kTokPerLoad * PA_MAX_LOADS_PER_UNIT;
+  static constexpr int kUnitsPerBlock = BS / kUnitTok;
+  static constexpr int kLoads = kUnitTok / kTokPerLoad;    // loads per unit (K, and V)
+  // units fetched together per wave: PA_KV_LOADS_IN_FLIGHT 16-byte loads per lane
   static constexpr int kUnroll =
       2 * kLoads >= PA_KV_LOADS_IN_FLIGHT ? 1 : PA_KV_LOADS_IN_FLIGHT / (2 * kLoads);
-  static_assert(D % kVec == 0 && kWave % kLanesPerTok == 0, "head_dim");
-  static_assert(BS % kTokPerLoad == 0, "block_size");
+  static_assert(D % kVec == 0 && kLanesPerTok <= kWave, "head_dim");
+  static_assert(BS % kUnitTok == 0 && kUnitTok % kTokPerLoad == 0, "block_size");
 };
 
 // Online-softmax state of one token row of one wave.
@@ -177,19 +196,22 @@ struct RowState {
   float acc[kVec];  // sum of 2^(z - m) * v over this lane's kVec dims
 };
 
-// Fold one block of one head into the row state.  kTail: only the first n_valid
-// tokens of the block are live; the others are skipped (never multiplied by zero,
-// because the slots past the end may hold anything, NaN included).
+// Fold one unit of one head into the row state.  kTail: only the first n_valid
+// tokens of the unit are live; the others are skipped (never multiplied by zero,
+// because the slots past the end may hold anything, NaN included).  `active`: this
+// lane holds data of its row (false only on the idle lanes of a padded row).
 template <typename T, int D, int BS, bool kTail>
-__device__ __forceinline__ void fold_block(RowState<Geometry<T, D, BS>::kVec>& st,
-                                           const u32x4& q, const u32x4* kr,
-                                           const u32x4* vr, float scale_log2,
-                                           int row, int n_valid) {
+__device__ __forceinline__ void fold_unit(RowState<Geometry<T, D, BS>::kVec>& st,
+                                          const u32x4& q, const u32x4* kr,
+                                          const u32x4* vr, float scale_log2,
+                                          int row, bool active, int n_valid) {
   using G = Geometry<T, D, BS>;
   float z[G::kLoads];
 #pragma unroll
   for (int i = 0; i < G::kLoads; ++i) {
-    z[i] = group_sum<G::kLanesPerTok>(Lane16<T>::dot(q, kr[i])) * scale_log2;
+    float part = Lane16<T>::dot(q, kr[i]);
+    if constexpr (G::kActive != G::kLanesPerTok) part = active ? part : 0.0f;
+    z[i] = group_sum<G::kLanesPerTok>(part) * scale_log2;
     if constexpr (kTail) {
       if (i * G::kTokPerLoad + row >= n_valid) z[i] = -INFINITY;
     }
@@ -202,7 +224,7 @@ __device__ __forceinline__ void fold_block(RowState<Geometry<T, D, BS>::kVec>& s
   if constexpr (kTail) {
     alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(st.m - m_new);
   } else {
-    alpha = fast_exp2(st.m - m_new);  // m_new is finite: every token of the block is live
+    alpha = fast_exp2(st.m - m_new);  // m_new is finite: every token of the unit is live
   }
   st.l *= alpha;
 #pragma unroll
@@ -232,71 +254,86 @@ __device__ __forceinline__ void merge_state(RowState<kVec>& a, float m_b, float 
   a.m = m;
 }
 
-// Fold this wave's blocks of one (partition, head) into its row state.  Lane j of
-// `ids` holds the physical id of the wave's j-th block (the first kWave of them);
-// a longer list is fetched kWave at a time from `my_table` (stride kWaves).
+// Element offset of unit u in the K (or V) pool, relative to the head's chunk of
+// block 0, for physical block `phys`.
 template <typename T, int D, int BS>
-__device__ __forceinline__ void attend_blocks(RowState<Geometry<T, D, BS>::kVec>& st,
-                                              const u32x4& q, int ids, const int* my_table,
-                                              const T* k_head, const T* v_head,
-                                              size_t block_stride, int lane_off, int lane,
-                                              int row, int n_mine, int n_full, int tail_valid,
-                                              float scale_log2) {
+__device__ __forceinline__ size_t unit_offset(int phys, int u, size_t block_stride) {
+  using G = Geometry<T, D, BS>;
+  size_t off = static_cast<size_t>(phys) * block_stride;
+  if constexpr (G::kUnitsPerBlock > 1) off += static_cast<size_t>(u % G::kUnitsPerBlock) * G::kUnitTok * D;
+  return off;
+}
+
+// Fold this wave's units of one (partition, head) into its row state.  The wave
+// owns units first_unit + j * kWaves, j < n_mine; the first n_full are whole.  Lane
+// j of `ids` holds the physical block of the wave's j-th unit (the first kWave of
+// them); a longer list is fetched kWave at a time from the table.
+template <typename T, int D, int BS>
+__device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>& st,
+                                             const u32x4& q, int ids, const int* table,
+                                             int first_unit, const T* k_head, const T* v_head,
+                                             size_t block_stride, int lane_off, int lane,
+                                             int row, bool active, int n_mine, int n_full,
+                                             int tail_valid, float scale_log2) {
   using G = Geometry<T, D, BS>;
   for (int base = 0; base < n_mine; base += kWave) {
     if (base > 0) {
       const int idx = base + lane;
-      ids = idx < n_mine ? my_table[idx * kWaves] : 0;
+      ids = idx < n_mine ? table[(first_unit + idx * kWaves) / G::kUnitsPerBlock] : 0;
     }
     const int chunk_full = min(max(n_full - base, 0), kWave);
     int j = 0;
-    // kUnroll full blocks per iteration, all loads issued before use
+    // kUnroll whole units per iteration, all loads issued before use
     for (; j + G::kUnroll <= chunk_full; j += G::kUnroll) {
       u32x4 kr[G::kUnroll][G::kLoads];
       u32x4 vr[G::kUnroll][G::kLoads];
 #pragma unroll
       for (int u = 0; u < G::kUnroll; ++u) {
         const int phys = __builtin_amdgcn_readlane(ids, j + u);
-        const T* kp = k_head + static_cast<size_t>(phys) * block_stride + lane_off;
+        const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j + u) * kWaves, block_stride);
+        const T* kp = k_head + off + lane_off;
 #pragma unroll
         for (int i = 0; i < G::kLoads; ++i) kr[u][i] = load_kv16(kp + i * G::kTokPerLoad * D);
       }
 #pragma unroll
       for (int u = 0; u < G::kUnroll; ++u) {
         const int phys = __builtin_amdgcn_readlane(ids, j + u);
-        const T* vp = v_head + static_cast<size_t>(phys) * block_stride + lane_off;
+        const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j + u) * kWaves, block_stride);
+        const T* vp = v_head + off + lane_off;
 #pragma unroll
         for (int i = 0; i < G::kLoads; ++i) vr[u][i] = load_kv16(vp + i * G::kTokPerLoad * D);
       }
 #pragma unroll
       for (int u = 0; u < G::kUnroll; ++u)
-        fold_block<T, D, BS, false>(st, q, kr[u], vr[u], scale_log2, row, BS);
+        fold_unit<T, D, BS, false>(st, q, kr[u], vr[u], scale_log2, row, active, G::kUnitTok);
     }
-    // remaining full blocks of this chunk, one at a time
+    // remaining whole units of this chunk, one at a time
     for (; j < chunk_full; ++j) {
       u32x4 kr[G::kLoads];
       u32x4 vr[G::kLoads];
       const int phys = __builtin_amdgcn_readlane(ids, j);
-      const T* kp = k_head + static_cast<size_t>(phys) * block_stride + lane_off;
-      const T* vp = v_head + static_cast<size_t>(phys) * block_stride + lane_off;
+      const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * kWaves, block_stride);
+      const T* kp = k_head + off + lane_off;
+      const T* vp = v_head + off + lane_off;
 #pragma unroll
       for (int i = 0; i < G::kLoads; ++i) kr[i] = load_kv16(kp + i * G::kTokPerLoad * D);
 #pragma unroll
       for (int i = 0; i < G::kLoads; ++i) vr[i] = load_kv16(vp + i * G::kTokPerLoad * D);
-      fold_block<T, D, BS, false>(st, q, kr, vr, scale_log2, row, BS);
+      fold_unit<T, D, BS, false>(st, q, kr, vr, scale_log2, row, active, G::kUnitTok);
     }
-    // the partly filled last block of the partition, if this chunk holds it
+    // the partly filled last unit of the partition, if this chunk holds it
     if (n_mine > n_full && base + j == n_full && j < kWave && base + j < n_mine) {
       u32x4 kr[G::kLoads];
       u32x4 vr[G::kLoads];
       const int phys = __builtin_amdgcn_readlane(ids, j);
-      const T* kp = k_head + static_cast<size_t>(phys) * block_stride + lane_off;
-      const T* vp = v_head + static_cast<size_t>(phys) * block_stride + lane_off;
+      const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * kWaves, block_stride);
+      const T* kp = k_head + off + lane_off;
+      const T* vp = v_head + off + lane_off;
 #pragma unroll
       for (int i = 0; i < G::kLoads; ++i) kr[i] = load_kv16(kp + i * G::kTokPerLoad * D);
 #pragma unroll
       for (int i = 0; i < G::kLoads; ++i) vr[i] = load_kv16(vp + i * G::kTokPerLoad * D);
-      fold_block<T, D, BS, true>(st, q, kr, vr, scale_log2, row, tail_valid);
+      fold_unit<T, D, BS, true>(st, q, kr, vr, scale_log2, row, active, tail_valid);
     }
   }
 }
@@ -336,22 +373,25 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
   const int P = prm.partition_tokens;
   const int start = prm.token_begin ? prm.token_begin[seq] : 0;  // a multiple of BS
   const int tok_begin = start + part * P;
-  const int blk_begin = tok_begin / BS;  // P is a multiple of BS
+  const int unit_begin = tok_begin / G::kUnitTok;  // P and start are multiples of BS
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int row = lane / G::kLanesPerTok;
   const int col = lane % G::kLanesPerTok;
+  const bool active = col < G::kActive;
+  const int col_data = active ? col : 0;  // idle lanes of a padded row read column 0
 
   // Issued together, before anything waits on memory: the context length, the
-  // query row and the ids of this wave's first kWave blocks.  The ids are bounded
+  // query row and the blocks of this wave's first kWave units.  The ids are bounded
   // by the table row, not by the context (entries past the context are read but
   // never used), so the K/V stream waits on one dependent load instead of two.
   const int* table = prm.block_tables + static_cast<size_t>(seq) * prm.max_blocks_per_seq;
-  const int* my_table = table + blk_begin + wave;
-  const int ids0 = blk_begin + wave + lane * kWaves < prm.max_blocks_per_seq ? my_table[lane * kWaves] : 0;
+  const int first_unit = unit_begin + wave;
+  const int blk0 = (first_unit + lane * kWaves) / G::kUnitsPerBlock;
+  const int ids0 = blk0 < prm.max_blocks_per_seq ? table[blk0] : 0;
   const u32x4 q = load16(static_cast<const T*>(prm.query) +
-                         (static_cast<size_t>(seq) * prm.num_heads + head) * D + col * kVec);
+                         (static_cast<size_t>(seq) * prm.num_heads + head) * D + col_data * kVec);
   const int ctx = prm.context_lens[seq];
   T* out_row = static_cast<T*>(prm.out) + (static_cast<size_t>(seq) * prm.num_heads + head) * D;
 
@@ -366,29 +406,29 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
     return;
   }
   const int tok_end = min(ctx, tok_begin + P);
-  const int full_end = tok_end / BS;  // blocks whose every token is live
-  const int blk_end = (tok_end + BS - 1) / BS;
+  const int full_end = tok_end / G::kUnitTok;  // units whose every token is live
+  const int unit_end = (tok_end + G::kUnitTok - 1) / G::kUnitTok;
 
   const size_t block_stride = static_cast<size_t>(prm.num_heads) * BS * D;  // elements
   const T* k_head = static_cast<const T*>(prm.key_cache) + static_cast<size_t>(head) * BS * D;
   const T* v_head = static_cast<const T*>(prm.value_cache) + static_cast<size_t>(head) * BS * D;
-  const int lane_off = row * D + col * kVec;  // element offset of this lane in load 0
+  const int lane_off = row * D + col_data * kVec;  // element offset of this lane in load 0
   const float scale_log2 = prm.scale * kLog2e;
 
-  // This wave owns logical blocks blk_begin + wave + j * kWaves, j < n_mine; the
-  // last of them may be partly filled.
-  const int n_total = blk_end - blk_begin;
+  // This wave owns units first_unit + j * kWaves, j < n_mine; the last of them may
+  // be partly filled.
+  const int n_total = unit_end - unit_begin;
   const int n_mine = n_total > wave ? (n_total - wave + kWaves - 1) / kWaves : 0;
-  const int n_full = full_end - blk_begin > wave ? (full_end - blk_begin - wave + kWaves - 1) / kWaves : 0;
-  const int tail_valid = tok_end - (blk_begin + wave + n_full * kWaves) * BS;
+  const int n_full = full_end - unit_begin > wave ? (full_end - unit_begin - wave + kWaves - 1) / kWaves : 0;
+  const int tail_valid = tok_end - (first_unit + n_full * kWaves) * G::kUnitTok;
 
   RowState<kVec> st;
   st.m = -INFINITY;
   st.l = 0.0f;
 #pragma unroll
   for (int j = 0; j < kVec; ++j) st.acc[j] = 0.0f;
-  attend_blocks<T, D, BS>(st, q, ids0, my_table, k_head, v_head, block_stride, lane_off, lane, row,
-                          n_mine, n_full, tail_valid, scale_log2);
+  attend_units<T, D, BS>(st, q, ids0, table, first_unit, k_head, v_head, block_stride, lane_off, lane,
+                         row, active, n_mine, n_full, tail_valid, scale_log2);
 
   // merge the token rows of the wave (lanes with the same col)
 #pragma unroll
@@ -405,7 +445,7 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
   __shared__ float s_m[kWaves];
   __shared__ float s_l[kWaves];
   __shared__ float s_o[kWaves][D];
-  if (row == 0) {
+  if (row == 0 && active) {
 #pragma unroll
     for (int j = 0; j < kVec; ++j) s_o[wave][col * kVec + j] = st.acc[j];
     if (col == 0) {
@@ -786,6 +826,9 @@ static hipError_t launch_partitions_d(const DecodeParams& prm, int block_size, h
     case 8: return launch_partitions_t<T, D, 8>(prm, stream);
     case 16: return launch_partitions_t<T, D, 16>(prm, stream);
     case 32: return launch_partitions_t<T, D, 32>(prm, stream);
+    case 64: return launch_partitions_t<T, D, 64>(prm, stream);
+    case 128: return launch_partitions_t<T, D, 128>(prm, stream);
+    case 256: return launch_partitions_t<T, D, 256>(prm, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -795,7 +838,10 @@ static hipError_t launch_partitions_dt(const DecodeParams& prm, int head_dim, in
                                        hipStream_t stream) {
   switch (head_dim) {
     case 64: return launch_partitions_d<T, 64>(prm, block_size, stream);
+    case 80: return launch_partitions_d<T, 80>(prm, block_size, stream);
+    case 96: return launch_partitions_d<T, 96>(prm, block_size, stream);
     case 128: return launch_partitions_d<T, 128>(prm, block_size, stream);
+    case 256: return launch_partitions_d<T, 256>(prm, block_size, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -806,18 +852,21 @@ hipError_t launch_decode_partitions(const DecodeParams& prm, bool f16, int head_
              : launch_partitions_dt<float>(prm, head_dim, block_size, stream);
 }
 
+template <typename T, int D>
+static void launch_reduce_td(const ReduceParams& prm, hipStream_t stream) {
+  dim3 grid(prm.num_heads, prm.num_seqs);
+  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), grid, dim3(D), 0, stream, prm);
+}
+
 template <typename T>
 static hipError_t launch_reduce_t(const ReduceParams& prm, int head_dim, hipStream_t stream) {
-  dim3 grid(prm.num_heads, prm.num_seqs);
   switch (head_dim) {
-    case 64:
-      hipLaunchKernelGGL((decode_reduce_kernel<T, 64>), grid, dim3(64), 0, stream, prm);
-      break;
-    case 128:
-      hipLaunchKernelGGL((decode_reduce_kernel<T, 128>), grid, dim3(128), 0, stream, prm);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: launch_reduce_td<T, 64>(prm, stream); break;
+    case 80: launch_reduce_td<T, 80>(prm, stream); break;
+    case 96: launch_reduce_td<T, 96>(prm, stream); break;
+    case 128: launch_reduce_td<T, 128>(prm, stream); break;
+    case 256: launch_reduce_td<T, 256>(prm, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -836,6 +885,15 @@ static hipError_t launch_prefix_d(const PrefixParams& prm, int block_size, hipSt
       break;
     case 32:
       hipLaunchKernelGGL((decode_prefix_kernel<D, 32>), grid, dim3(kPrefixThreads), 0, stream, prm);
+      break;
+    case 64:
+      hipLaunchKernelGGL((decode_prefix_kernel<D, 64>), grid, dim3(kPrefixThreads), 0, stream, prm);
+      break;
+    case 128:
+      hipLaunchKernelGGL((decode_prefix_kernel<D, 128>), grid, dim3(kPrefixThreads), 0, stream, prm);
+      break;
+    case 256:
+      hipLaunchKernelGGL((decode_prefix_kernel<D, 256>), grid, dim3(kPrefixThreads), 0, stream, prm);
       break;
     default:
       return hipErrorInvalidValue;

@@ -82,8 +82,10 @@ def _bad_decode(ops, **over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(D=80), 3),
+    (dict(D=72), 3),
+    (dict(D=512), 3),
     (dict(bs=12), 3),
+    (dict(bs=512), 3),
     (dict(dtype=7), 3),
     (dict(maxctx=65), 2),          # more than max_blocks_per_seq * block_size
     (dict(NB=0), 2),
@@ -112,7 +114,8 @@ def test_append_and_copy_reject_bad_arguments(ops):
     assert lib.pa_cache_append(p, p, p, None, p, 4, 4, 64, 16, 64, 0, None) == 1
     assert lib.pa_cache_append(p, p, p, p, p, -1, 4, 64, 16, 64, 0, None) == 2
     assert lib.pa_cache_append(None, None, None, None, None, 0, 4, 64, 16, 64, 0, None) == 0
-    assert lib.pa_block_copy(p, p, p, 2, 4, 96, 16, 64, 0, None) == 3
+    assert lib.pa_block_copy(p, p, p, 2, 4, 72, 16, 64, 0, None) == 3
+    assert lib.pa_block_copy(p, p, p, 2, 4, 64, 24, 64, 0, None) == 3
     assert lib.pa_block_copy(p, None, p, 2, 4, 64, 16, 64, 0, None) == 1
     assert lib.pa_block_copy(None, None, None, 0, 4, 64, 16, 64, 0, None) == 0
 

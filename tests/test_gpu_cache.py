@@ -25,7 +25,8 @@ def _bits(a):
 
 
 CASES = [(np.float16, 128, 16, 32), (np.float16, 64, 32, 4), (np.float16, 128, 8, 7),
-         (np.float32, 64, 16, 4), (np.float32, 128, 32, 3)]
+         (np.float32, 64, 16, 4), (np.float32, 128, 32, 3), (np.float16, 80, 64, 5),
+         (np.float16, 256, 256, 2), (np.float32, 96, 128, 3)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{np.dtype(c[0]).name}-D{c[1]}-bs{c[2]}-H{c[3]}")

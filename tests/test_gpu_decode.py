@@ -60,6 +60,18 @@ MID_CASES = [
     (np.float32, 128, 32, (1, 500), 0),
     (np.float32, 64, 8, (1, 200), 24),
     (np.float32, 64, 32, (1, 700), 160),
+    # head dims whose rows do not fill a power of two of lanes, and large blocks
+    # walked in several units per block
+    (np.float16, 80, 16, (1, 700), 64),
+    (np.float16, 96, 32, (1, 900), 0),
+    (np.float16, 256, 16, (1, 600), 128),
+    (np.float16, 128, 64, (1, 1500), 256),
+    (np.float16, 128, 128, (1, 2000), 512),
+    (np.float16, 64, 256, (1, 3000), 0),
+    (np.float16, 256, 256, (300, 2000), 512),
+    (np.float32, 80, 8, (1, 300), 0),
+    (np.float32, 256, 64, (1, 700), 128),
+    (np.float32, 96, 128, (100, 900), 256),
 ]
 
 

@@ -61,6 +61,8 @@ CASES = [
     ("wide", 64, 32, [33], (1, 3), (5, 50), 0, 0, 0),
     ("long", 128, 16, [4, 4, 4, 4, 4, 4], (10, 40), (1, 300), 1, 0, 64),
     ("no_groups", 128, 16, [], (0, 0), (1, 200), 5, 0, 0),
+    ("bs64", 128, 64, [8, 3], (1, 5), (1, 150), 1, 0, 0),
+    ("bs256", 64, 256, [6], (1, 2), (1, 300), 0, 0, 256),
 ]
 
 

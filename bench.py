@@ -301,6 +301,32 @@ def graph_step(torch, ops, metrics, args):
     return rows
 
 
+def swap_throughput(torch, ops, args, pairs=2048):
+    """pa_swap_blocks of ``pairs`` Llama-shaped blocks (32 heads x 16 x 128 fp16:
+    128 KiB of K and 128 KiB of V each) from the GPU pool to a pinned host pool and
+    back: bytes moved / time, each direction."""
+    log(args, "block swap")
+    shape = (pairs, 32, 16, 128)
+    gk = torch.randn(shape, dtype=torch.float16, device="cuda")
+    gv = torch.randn(shape, dtype=torch.float16, device="cuda")
+    hk = torch.empty(shape, dtype=torch.float16, pin_memory=True)
+    hv = torch.empty(shape, dtype=torch.float16, pin_memory=True)
+    ids = torch.randperm(pairs, generator=torch.Generator().manual_seed(3))
+    out_pairs = torch.stack([torch.arange(pairs), ids], dim=1).to(torch.int32).cuda()
+    in_pairs = torch.stack([ids, torch.arange(pairs)], dim=1).to(torch.int32).cuda()
+    moved = 2 * pairs * 32 * 16 * 128 * 2
+    res = {"pairs": pairs, "bytes_each_way": moved}
+    for name, fn in (("out", lambda: ops.pa_swap_blocks(hk, hv, gk, gv, out_pairs)),
+                     ("in", lambda: ops.pa_swap_blocks(gk, gv, hk, hv, in_pairs))):
+        fn()
+        ms = time_launches(fn, 5, torch)
+        res[f"swap_{name}_ms"] = round(ms, 4)
+        res[f"swap_{name}_gbps"] = round(moved / (ms * 1e-3) / 1e9, 2)
+    del gk, gv, hk, hv
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_probe(torch, ops, metrics, pairs=1024):
     """One pa_block_copy of ``pairs`` blocks of 32 heads x 16 x 128 fp16 (128 KiB per
     block for K and for V): a plain copy of known size, run once, whose memory
@@ -429,6 +455,7 @@ def main():
         record["long_context"] = long_context_decode(torch, ops, metrics, args)
         record["shared_prefix_decode"] = shared_prefix_decode(torch, ops, metrics, args)
         record["graph_step"] = graph_step(torch, ops, metrics, args)
+        record["block_swap"] = swap_throughput(torch, ops, args)
     if args.mixes:
         record["step_mixes"] = {
             "continuous_batching": run_mix("ContinuousBatching", 3, torch, args),

@@ -218,6 +218,29 @@ pa_status pa_block_copy(void* key_cache, void* value_cache, const int32_t* block
                         void* stream);
 
 /*
+ * pa_swap_blocks -- move whole blocks between two pools that may live in different
+ * memories: under memory pressure a scheduler moves the blocks of preempted
+ * sequences out of the GPU pool into host memory and brings them back when the
+ * sequences resume ([Reading vLLM] §3, blocks_to_swap_out / blocks_to_swap_in).
+ * For each pair (src, dst) of block_pairs:
+ *     dst_key[dst] = src_key[src];  dst_value[dst] = src_value[src]
+ * (all heads and slots, bits unchanged).  Both pools have the layout
+ * [num_blocks, num_heads, block_size, head_dim] (src_num_blocks and dst_num_blocks
+ * blocks).  Each pool pointer, and block_pairs (int32 [num_pairs, 2]), must be
+ * device memory or pinned host memory (hipHostMalloc; torch pin_memory=True): the
+ * library asks the runtime for every pointer and refuses anything else (pageable
+ * memory) with PA_ERR_INVALID_ARG before enqueuing.  The copy runs on the GPU and
+ * reads or writes host memory across the host link.  Destinations must be distinct
+ * and, when both sides are one pool, never a source; ids must lie in their pools
+ * (caller preconditions).
+ */
+pa_status pa_swap_blocks(void* dst_key, void* dst_value, const void* src_key,
+                         const void* src_value, const int32_t* block_pairs, int32_t num_pairs,
+                         int32_t num_heads, int32_t head_dim, int32_t block_size,
+                         int32_t src_num_blocks, int32_t dst_num_blocks, pa_dtype dtype,
+                         void* stream);
+
+/*
  * Shared-prefix decode.
  *
  * Sequences may share their leading blocks by reference count, e.g. the prompt of

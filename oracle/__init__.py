@@ -18,6 +18,7 @@ from .paged_attention import (  # noqa: F401
     partition_state,
     slot_of,
     slots_for_positions,
+    swap_blocks,
     to_float64,
     token_location,
 )

@@ -251,6 +251,26 @@ def block_copy(k_pool, v_pool, pairs, inplace=False):
     return k_out, v_out
 
 
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, inplace=False):
+    """Destination pools with block dst := source block src for each (src, dst):
+    copies, or the given destination arrays themselves when ``inplace``.
+
+    Moving blocks between the GPU pool and host memory under memory pressure and
+    back ([Reading vLLM] §3, blocks_to_swap_out / blocks_to_swap_in) copies whole
+    blocks, K and V, unchanged.  The two pools may differ in block count.
+    Destinations must be distinct."""
+    pairs = [(int(a), int(b)) for a, b in np.asarray(pairs).reshape(-1, 2)]
+    dsts = [b for _, b in pairs]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("swap destinations repeat")
+    k_out = dst_k if inplace else dst_k.copy()
+    v_out = dst_v if inplace else dst_v.copy()
+    for a, b in pairs:
+        k_out[b] = src_k[a]
+        v_out[b] = src_v[a]
+    return k_out, v_out
+
+
 def slots_for_positions(block_tables, seq_ids, positions, block_size):
     """Slot of (sequence, position) pairs, recomputed from the tables alone."""
     return np.array([slot_of(block_tables[s], p, block_size)

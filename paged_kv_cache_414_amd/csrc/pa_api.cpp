@@ -76,6 +76,20 @@ pa_status check_dtype_shape(pa_dtype dtype, int32_t head_dim, int32_t block_size
 
 int32_t round_up(int64_t x, int32_t m) { return static_cast<int32_t>(((x + m - 1) / m) * m); }
 
+// The address a kernel can use for `p`, or nullptr when `p` is neither device
+// memory nor pinned host memory mapped into the GPU (pageable host memory, unknown
+// addresses): such pointers are refused on the host, never handed to a kernel.
+const void* device_visible(const void* p) {
+  if (!p) return nullptr;
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeHost) return nullptr;
+  return attr.devicePointer;
+}
+
 // Resolved partition length, or -1 with the last error set.
 int32_t resolve_partition(int32_t num_seqs, int32_t num_heads, int32_t block_size,
                           int32_t max_context_len, int32_t partition_size) {
@@ -419,12 +433,47 @@ pa_status pa_block_copy(void* key_cache, void* value_cache, const int32_t* block
   if (!aligned16(key_cache) || !aligned16(value_cache))
     return fail(PA_ERR_INVALID_ARG, "caches must be 16-byte aligned");
   pa::CopyParams prm;
-  prm.key_cache = key_cache;
-  prm.value_cache = value_cache;
+  prm.src_key = key_cache;
+  prm.src_value = value_cache;
+  prm.dst_key = key_cache;
+  prm.dst_value = value_cache;
   prm.block_pairs = block_pairs;
   prm.num_pairs = num_pairs;
   prm.block_bytes = static_cast<int64_t>(num_heads) * block_size * head_dim * static_cast<int64_t>(elem_bytes(dtype));
   return from_hip(pa::launch_block_copy(prm, static_cast<hipStream_t>(stream)), "block copy launch");
+}
+
+pa_status pa_swap_blocks(void* dst_key, void* dst_value, const void* src_key, const void* src_value,
+                         const int32_t* block_pairs, int32_t num_pairs, int32_t num_heads, int32_t head_dim,
+                         int32_t block_size, int32_t src_num_blocks, int32_t dst_num_blocks, pa_dtype dtype,
+                         void* stream) {
+  pa_status st = check_dtype_shape(dtype, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0 || num_heads <= 0 || src_num_blocks <= 0 || dst_num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_pairs %d >= 0, num_heads %d > 0 and pool sizes %d, %d > 0 required",
+                num_pairs, num_heads, src_num_blocks, dst_num_blocks);
+  if (num_pairs == 0) return ok();
+  if (!dst_key || !dst_value || !src_key || !src_value || !block_pairs)
+    return fail(PA_ERR_NULL, "a required pointer is NULL (dst_key, dst_value, src_key, src_value, block_pairs)");
+  if (!aligned16(dst_key) || !aligned16(dst_value) || !aligned16(src_key) || !aligned16(src_value))
+    return fail(PA_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+  const void* ptrs[5] = {dst_key, dst_value, src_key, src_value, block_pairs};
+  const void* dev[5];
+  static const char* const names[5] = {"dst_key", "dst_value", "src_key", "src_value", "block_pairs"};
+  for (int i = 0; i < 5; ++i) {
+    dev[i] = device_visible(ptrs[i]);
+    if (!dev[i])
+      return fail(PA_ERR_INVALID_ARG, "%s is neither device memory nor pinned host memory", names[i]);
+  }
+  pa::CopyParams prm;
+  prm.dst_key = const_cast<void*>(dev[0]);
+  prm.dst_value = const_cast<void*>(dev[1]);
+  prm.src_key = dev[2];
+  prm.src_value = dev[3];
+  prm.block_pairs = static_cast<const int32_t*>(dev[4]);
+  prm.num_pairs = num_pairs;
+  prm.block_bytes = static_cast<int64_t>(num_heads) * block_size * head_dim * static_cast<int64_t>(elem_bytes(dtype));
+  return from_hip(pa::launch_block_copy(prm, static_cast<hipStream_t>(stream)), "block swap launch");
 }
 
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,

@@ -788,7 +788,9 @@ __global__ __launch_bounds__(256) void cache_append_kernel(AppendParams prm) {
 }
 
 // ---------------------------------------------------------------------------------
-// block copy: grid (pairs, chunk groups of a block); 16 bytes per thread per step
+// block copy between pools (the same pool for copy-on-write, the GPU pool and a
+// pinned host pool for swapping): grid (pairs, chunk groups of a block); 16 bytes
+// per thread per step
 // ---------------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void block_copy_kernel(CopyParams prm) {
@@ -796,10 +798,10 @@ __global__ __launch_bounds__(256) void block_copy_kernel(CopyParams prm) {
   const int src = prm.block_pairs[2 * pair];
   const int dst = prm.block_pairs[2 * pair + 1];
   const int64_t chunks = prm.block_bytes / 16;
-  const char* ks = static_cast<const char*>(prm.key_cache) + static_cast<size_t>(src) * prm.block_bytes;
-  const char* vs = static_cast<const char*>(prm.value_cache) + static_cast<size_t>(src) * prm.block_bytes;
-  char* kd = static_cast<char*>(prm.key_cache) + static_cast<size_t>(dst) * prm.block_bytes;
-  char* vd = static_cast<char*>(prm.value_cache) + static_cast<size_t>(dst) * prm.block_bytes;
+  const char* ks = static_cast<const char*>(prm.src_key) + static_cast<size_t>(src) * prm.block_bytes;
+  const char* vs = static_cast<const char*>(prm.src_value) + static_cast<size_t>(src) * prm.block_bytes;
+  char* kd = static_cast<char*>(prm.dst_key) + static_cast<size_t>(dst) * prm.block_bytes;
+  char* vd = static_cast<char*>(prm.dst_value) + static_cast<size_t>(dst) * prm.block_bytes;
   for (int64_t c = static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x; c < chunks;
        c += static_cast<int64_t>(gridDim.y) * blockDim.x) {
     const u32x4 k = load16(ks + c * 16);

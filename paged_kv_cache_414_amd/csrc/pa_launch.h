@@ -79,8 +79,10 @@ struct AppendParams {
 };
 
 struct CopyParams {
-  void* key_cache;
-  void* value_cache;
+  const void* src_key;  // source pool (block ids: first of each pair)
+  const void* src_value;
+  void* dst_key;        // destination pool (second of each pair); may be the source pool
+  void* dst_value;
   const int32_t* block_pairs;
   int32_t num_pairs;
   int64_t block_bytes;  // heads * block_size * head_dim * element size

@@ -41,6 +41,7 @@ SIGNATURES = {
                                _vp]),
     "pa_block_copy": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32] * 9),
+    "pa_swap_blocks": (_i32, [_vp] * 5 + [_i32] * 7 + [_vp]),
     # host block manager (include/pa_blocks.h)
     "pa_bm_create": (_vp, [_i32, _i32, ctypes.c_uint64]),
     "pa_bm_destroy": (None, [_vp]),
@@ -301,3 +302,27 @@ def pa_decode_shared_prefix(out, query, key_cache, value_cache, block_tables, co
                                        part, int(prefix_partition_size), p_ws, ws_bytes,
                                        _stream(stream, dev) if stream is not None else strm))
     return out
+
+
+# ----------------------------------------------------------------------------------
+# block swap between the GPU pool and a pinned host pool
+# ----------------------------------------------------------------------------------
+
+def pa_swap_blocks(dst_key, dst_value, src_key, src_value, block_pairs, stream=None):
+    """dst[pair[1]] = src[pair[0]] for K and V, pools in device or pinned host memory
+    (see include/pa.h); ``block_pairs`` int32 [n, 2] on the GPU or pinned."""
+    _int32(block_pairs)
+    if not (dst_key.dtype == dst_value.dtype == src_key.dtype == src_value.dtype):
+        raise ValueError("pools must share one dtype")
+    nb_d, h, bs, d = dst_key.shape
+    nb_s = src_key.shape[0]
+    if src_key.shape[1:] != dst_key.shape[1:] or src_value.shape != src_key.shape or \
+            dst_value.shape != dst_key.shape:
+        raise ValueError("pools must be [num_blocks, H, bs, D] with equal H, bs, D")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2]")
+    gpu = next((t.device for t in (dst_key, src_key, block_pairs) if t.device.type == "cuda"),
+               torch.device("cuda", torch.cuda.current_device()))
+    _check(lib.pa_swap_blocks(_ptr(dst_key), _ptr(dst_value), _ptr(src_key), _ptr(src_value),
+                              _ptr(block_pairs), block_pairs.shape[0], h, d, bs, nb_s, nb_d,
+                              _dtype(dst_key), _stream(stream, gpu)))

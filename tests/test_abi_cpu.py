@@ -171,3 +171,16 @@ def test_shared_prefix_planning(ops):
     assert ops.lib.pa_last_error() != b""
     with pytest.raises(ops.PagedAttentionError):
         ops.pa_decode_shared_prefix_workspace_bytes(s, h, d, 16, 8, 1000, 272)
+
+
+def test_swap_rejects_bad_arguments(ops):
+    lib = ops.lib
+    p = 1 << 20
+    # dtype, shape, sizes and NULLs are checked before any pointer is looked up
+    assert lib.pa_swap_blocks(p, p, p, p, p, 2, 4, 64, 16, 8, 8, 5, None) == 3
+    assert lib.pa_swap_blocks(p, p, p, p, p, 2, 4, 72, 16, 8, 8, 0, None) == 3
+    assert lib.pa_swap_blocks(p, p, p, p, p, -1, 4, 64, 16, 8, 8, 0, None) == 2
+    assert lib.pa_swap_blocks(p, p, p, p, p, 2, 4, 64, 16, 0, 8, 0, None) == 2
+    assert lib.pa_swap_blocks(p, None, p, p, p, 2, 4, 64, 16, 8, 8, 0, None) == 1
+    assert lib.pa_swap_blocks(p + 4, p, p, p, p, 2, 4, 64, 16, 8, 8, 0, None) == 2
+    assert lib.pa_swap_blocks(None, None, None, None, None, 0, 4, 64, 16, 8, 8, 0, None) == 0

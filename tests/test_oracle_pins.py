@@ -294,3 +294,56 @@ def test_planted_append_mistake_is_caught(fn):
 def test_planted_copy_mistake_is_caught():
     with pytest.raises(Exception):
         check_block_copy(_copy_k_only)
+
+
+# ----------------------------------------------------------------------------------
+# swapping blocks between two pools ("Reading the vLLM source" §3)
+# ----------------------------------------------------------------------------------
+
+def _labelled_pool(num_blocks, offset):
+    """Pools whose every element names its block: K = offset + id, V = -(offset + id)."""
+    ids = np.arange(num_blocks, dtype=np.float32)[:, None, None, None] + offset
+    k = np.broadcast_to(ids, (num_blocks, 2, 4, 8)).astype(np.float32).copy()
+    return k, -k
+
+
+def check_swap(swap_fn):
+    """Device pool of 12 blocks (labels 0..11), host pool of 6 (labels 100..105):
+    swapping out (src in the device pool, dst in the host pool) leaves host block dst
+    labelled with device id src, everything else untouched; swapping back in restores
+    the device pool."""
+    dk, dv = _labelled_pool(12, 0.0)
+    hk, hv = _labelled_pool(6, 100.0)
+    out_pairs = np.array([[7, 0], [2, 5], [11, 3]], dtype=np.int32)
+    hk2, hv2 = swap_fn(hk, hv, dk, dv, out_pairs)
+    want = {0: 7.0, 5: 2.0, 3: 11.0, 1: 101.0, 2: 102.0, 4: 104.0}
+    for blk, label in want.items():
+        assert np.all(hk2[blk] == label) and np.all(hv2[blk] == -label), blk
+    # the device blocks are reused by someone else, then the data comes back in
+    dk_reused, dv_reused = np.zeros_like(dk), np.zeros_like(dv)
+    back = out_pairs[:, ::-1].copy()  # (host, device)
+    dk3, dv3 = swap_fn(dk_reused, dv_reused, hk2, hv2, back)
+    for dev_blk in (7, 2, 11):
+        assert np.array_equal(dk3[dev_blk], dk[dev_blk]) and np.array_equal(dv3[dev_blk], dv[dev_blk])
+    assert np.all(dk3[[0, 1, 3, 4, 5, 6, 8, 9, 10]] == 0)
+
+
+def test_swap_blocks_pins():
+    check_swap(oracle.swap_blocks)
+    with pytest.raises(ValueError):
+        oracle.swap_blocks(*_labelled_pool(4, 0.0), *_labelled_pool(4, 9.0), [[0, 1], [2, 1]])
+
+
+def _swap_reversed(dst_k, dst_v, src_k, src_v, pairs):
+    return oracle.swap_blocks(dst_k, dst_v, src_k, src_v, np.asarray(pairs)[:, ::-1])
+
+
+def _swap_k_only(dst_k, dst_v, src_k, src_v, pairs):
+    k, _ = oracle.swap_blocks(dst_k, dst_v, src_k, src_v, pairs)
+    return k, dst_v.copy()
+
+
+@pytest.mark.parametrize("fn", [_swap_reversed, _swap_k_only])
+def test_planted_swap_mistake_is_caught(fn):
+    with pytest.raises(Exception):
+        check_swap(fn)

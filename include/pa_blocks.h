@@ -61,6 +61,13 @@ pa_status pa_bm_ref_counts(const pa_block_manager* bm, int32_t* ref_counts);
 pa_status pa_bm_add_sequence(pa_block_manager* bm, int64_t seq_id, int32_t num_tokens,
                              int32_t* slots);
 
+/* Admit n sequences at once (seq_ids[n], num_tokens[n]), in order; slots (may be
+ * NULL) receives every prompt token's slot, the sequences' runs concatenated in
+ * order.  All or nothing: PA_ERR_OUT_OF_BLOCKS (nothing changed) if the blocks of
+ * all of them do not fit; PA_ERR_INVALID_ARG for an existing or repeated id. */
+pa_status pa_bm_add_sequences(pa_block_manager* bm, const int64_t* seq_ids,
+                              const int32_t* num_tokens, int32_t n, int32_t* slots);
+
 /* child_id holds every block of parent_id (reference counts + 1) and its length. */
 pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id);
 

@@ -110,6 +110,17 @@ class BlockManager:
         self._check(self._lib.pa_bm_add_sequence(self._h, int(seq_id), n, _ptr(out)))
         return out[:n]
 
+    def add_sequences(self, seq_ids, num_tokens, slots: np.ndarray | None = None) -> np.ndarray:
+        """Admit several sequences at once (all or nothing); returns their prompt
+        tokens' slots, concatenated in order (written into ``slots`` when given)."""
+        ids = _ids(seq_ids)
+        lens = np.ascontiguousarray(np.asarray(num_tokens, dtype=np.int32).reshape(-1))
+        total = int(lens.sum())
+        out = np.empty(max(total, 1), dtype=np.int32) if slots is None else slots
+        self._check(self._lib.pa_bm_add_sequences(self._h, _ptr(ids), _ptr(lens), ids.size,
+                                                  _ptr(out)))
+        return out[:total]
+
     def fork(self, parent_id: int, child_id: int) -> None:
         """The child shares every block of the parent (reference counts + 1)."""
         self._check(self._lib.pa_bm_fork(self._h, int(parent_id), int(child_id)))

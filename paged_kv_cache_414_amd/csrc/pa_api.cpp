@@ -49,12 +49,14 @@ pa_status from_hip(hipError_t err, const char* what) {
 
 // Library choice of the partition length: start from the whole longest context
 // (one partition per sequence, no merge pass) and halve while the launch would hold
-// fewer than kAutoMinUnits (sequence, head, partition) work units, i.e. about twelve
-// workgroups per compute unit of a 256-CU MI355X, as long as the half stays at or
-// above kAutoMinPartitionTokens.  Measured on MI355X: long partitions stream at a higher
-// rate (less per-workgroup set-up and fewer short tail partitions) as long as the
-// grid keeps every CU busy.
-constexpr int64_t kAutoMinUnits = 3072;
+// fewer than kAutoMinUnits (sequence, head, partition) workgroups -- two per compute
+// unit of a 256-CU MI355X -- as long as the half stays at or above
+// kAutoMinPartitionTokens.  Measured on MI355X (fp16, 32 heads x 128): few long
+// workgroups stream fastest as long as there are at least about two per CU; e.g. 64
+// sequences of contexts up to 562 tokens: one partition 47.7 us, two 54.5 us; 8
+// sequences of 16K-32K tokens: 512 workgroups 6.55 TB/s, 4096 workgroups 6.25 TB/s,
+// 256 workgroups 6.52 TB/s, but 4 sequences at 128 workgroups only 5.55 TB/s.
+constexpr int64_t kAutoMinUnits = 512;
 constexpr int32_t kAutoMinPartitionTokens = 256;
 constexpr int32_t kMaxGridYZ = 65535;
 

@@ -143,6 +143,31 @@ pa_status pa_bm_add_sequence(pa_block_manager* bm, int64_t seq_id, int32_t num_t
   return pa::clear_error();
 }
 
+pa_status pa_bm_add_sequences(pa_block_manager* bm, const int64_t* seq_ids, const int32_t* num_tokens,
+                              int32_t n, int32_t* slots) {
+  if (!bm) return pa::set_error(PA_ERR_NULL, "manager is NULL");
+  if (n < 0) return pa::set_error(PA_ERR_INVALID_ARG, "n %d is negative", n);
+  if (n > 0 && (!seq_ids || !num_tokens)) return pa::set_error(PA_ERR_NULL, "seq_ids and num_tokens must not be NULL");
+  int64_t needed = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (num_tokens[i] < 0) return pa::set_error(PA_ERR_INVALID_ARG, "num_tokens[%d] = %d is negative", i, num_tokens[i]);
+    if (bm->seqs.count(seq_ids[i])) return pa::set_error(PA_ERR_INVALID_ARG, "sequence %lld exists", (long long)seq_ids[i]);
+    for (int32_t j = 0; j < i; ++j) {
+      if (seq_ids[j] == seq_ids[i])
+        return pa::set_error(PA_ERR_INVALID_ARG, "sequence %lld listed twice", (long long)seq_ids[i]);
+    }
+    needed += blocks_for(num_tokens[i], bm->block_size);
+  }
+  if (needed > static_cast<int64_t>(bm->free_list.size()))
+    return pa::set_error(PA_ERR_OUT_OF_BLOCKS, "%lld blocks needed, %zu free", (long long)needed, bm->free_list.size());
+  int64_t cursor = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    pa_bm_add_sequence(bm, seq_ids[i], num_tokens[i], slots ? slots + cursor : nullptr);
+    cursor += num_tokens[i];
+  }
+  return pa::clear_error();
+}
+
 pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id) {
   if (!bm) return pa::set_error(PA_ERR_NULL, "manager is NULL");
   auto it = bm->seqs.find(parent_id);

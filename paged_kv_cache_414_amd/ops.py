@@ -49,6 +49,7 @@ SIGNATURES = {
     "pa_bm_can_allocate": (_i32, [_vp, _i32]),
     "pa_bm_ref_counts": (_i32, [_vp, _vp]),
     "pa_bm_add_sequence": (_i32, [_vp, ctypes.c_int64, _i32, _vp]),
+    "pa_bm_add_sequences": (_i32, [_vp, _vp, _vp, _i32, _vp]),
     "pa_bm_fork": (_i32, [_vp, ctypes.c_int64, ctypes.c_int64]),
     "pa_bm_free": (_i32, [_vp, ctypes.c_int64]),
     "pa_bm_append_slots": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
@@ -97,9 +98,18 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return t.data_ptr() if t.numel() else None
 
 
+try:  # the current stream's raw handle without building a Stream object
+    _raw_stream = torch._C._cuda_getCurrentRawStream
+except AttributeError:  # pragma: no cover
+    _raw_stream = None
+
+
 def _stream(stream, device) -> int | None:
     if stream is None:
-        stream = torch.cuda.current_stream(device)
+        index = device if isinstance(device, int) else device.index
+        if _raw_stream is not None:
+            return _raw_stream(index)
+        stream = torch.cuda.current_stream(index)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -110,10 +120,11 @@ def _dtype(t: torch.Tensor) -> int:
         raise ValueError(f"unsupported dtype {t.dtype} (float32 or float16)") from None
 
 
-def _same_device(*ts):
-    devs = {t.device for t in ts if t is not None}
-    if len(devs) != 1 or next(iter(devs)).type != "cuda":
-        raise ValueError(f"all tensors must be on one GPU, got {devs}")
+def _same_device(*ts) -> int:
+    """Index of the one GPU all tensors live on."""
+    devs = {t.get_device() for t in ts if t is not None}
+    if len(devs) != 1 or next(iter(devs)) < 0:
+        raise ValueError(f"all tensors must be on one GPU, got {[t.device for t in ts if t is not None]}")
     return next(iter(devs))
 
 

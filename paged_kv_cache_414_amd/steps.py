@@ -65,6 +65,7 @@ class StepInputs:
     new_v: np.ndarray
     q: np.ndarray
     prompt_lens: np.ndarray | None = None  # sequences admitted after the step
+    finishing: np.ndarray | None = None  # batch rows that finish after the step
     prompt_k: np.ndarray | None = None
     prompt_v: np.ndarray | None = None
     dev: tuple | None = None  # (new_k, new_v, q, prompt_k, prompt_v) on the device
@@ -187,16 +188,12 @@ class StepMix:
         self.next_id += 1
         return self.next_id - 1
 
-    def _admit(self, lens, slots_out: np.ndarray) -> list:
-        """Admit one sequence per entry of ``lens``; their prompt slots are written
-        into ``slots_out`` in admission order."""
-        ids, cursor = [], 0
-        for n in lens:
-            n = int(n)
-            sid = self._new_id()
-            self.manager.add_sequence(sid, n, slots=slots_out[cursor:cursor + max(n, 1)])
-            cursor += n
-            ids.append(sid)
+    def _admit(self, lens, slots_out: np.ndarray) -> np.ndarray:
+        """Admit one sequence per entry of ``lens`` (one native call); their prompt
+        slots are written into ``slots_out`` in admission order."""
+        ids = np.arange(self.next_id, self.next_id + len(lens), dtype=np.int64)
+        self.next_id += len(lens)
+        self.manager.add_sequences(ids, lens, slots=slots_out)
         return ids
 
     def _write_rows(self, slots_d, k_rows, v_rows):
@@ -296,6 +293,7 @@ class ContinuousBatching(StepMix):
     def _draw_inputs(self, k: int) -> StepInputs:
         inp = super()._draw_inputs(k)
         inp.prompt_lens = self.draws.replacement_prompt_lens(k)
+        inp.finishing = self.draws.finishing(k)
         inp.prompt_k, inp.prompt_v = self.draws.prompt_kv(k, inp.prompt_lens)
         return inp
 
@@ -304,7 +302,7 @@ class ContinuousBatching(StepMix):
         # finished sequences can be reused by the new prompts, which are written
         # after the decode in stream order
         inp = self.inputs(k_step)
-        finishing = self.draws.finishing(k_step)
+        finishing = inp.finishing
         for lane in finishing:
             self.manager.free(int(self.lanes[lane]))
         total = int(inp.prompt_lens.sum())

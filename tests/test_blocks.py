@@ -232,3 +232,21 @@ def test_randomized_invariants():
             ids = sorted(length)
             assert m.context_lens(ids).tolist() == [length[s] for s in ids]
     assert copies_seen > 0
+
+
+def test_batch_admission_is_all_or_nothing():
+    m = blocks.BlockManager(10, 16)
+    slots = m.add_sequences([0, 1, 2], [20, 0, 33])
+    assert len(slots) == 53
+    assert slots[:20].tolist() == [m.slot(0, p) for p in range(20)]
+    assert slots[20:].tolist() == [m.slot(2, p) for p in range(33)]
+    assert m.num_free == 10 - 2 - 0 - 3
+    before = m.num_free
+    with pytest.raises(blocks.OutOfBlocks):
+        m.add_sequences([3, 4], [48, 48])  # 6 blocks > 5 free
+    assert m.num_free == before and m.blocks_needed(48) == 3
+    with pytest.raises(ValueError):
+        m.add_sequences([5, 5], [1, 1])  # listed twice
+    with pytest.raises(ValueError):
+        m.add_sequences([6, 0], [1, 1])  # 0 exists
+    assert m.num_free == before

@@ -531,11 +531,12 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(ReduceParams prm) {
 // A group is a range of sequences whose first prefix_len tokens live in the same
 // physical blocks (shared by reference count).  Each shared block is read once for
 // all of the group's queries, so the score and value products become small dense
-// matrix products, run on the matrix cores as v_mfma_f32_16x16x16_f16 tiles of 16
-// tokens x 16 queries:
-//   scores  S^T[t][g] = sum_d K[t][d] Q[g][d]   (A = K tile, B = Q^T; lane l holds
-//           token l%16 of K and query l%16 of Q, both over the same dims)
-//   output  O^T[d][g] = sum_t V[t][d] P[g][t]   (A = V^T, B = P^T)
+// matrix products, run on the matrix cores as tiles of 16 tokens x 16 queries:
+//   scores  S^T[t][g] = sum_d K[t][d] Q[g][d]   (v_mfma_f32_16x16x32_f16, A = K tile,
+//           B = Q^T; lane l holds token l%16 of K and query l%16 of Q, both over the
+//           same 8 dims per step: [32c + 8(l/16), +8) at step c)
+//   output  O^T[d][g] = sum_t V[t][d] P[g][t]   (v_mfma_f32_16x16x16_f16, A = V^T,
+//           B = P^T)
 // The matrix-core result layout puts tokens 4(l/16)..+3 of query l%16 in lane l,
 // which is exactly the B operand layout of the value product, so the softmax
 // weights never leave their lanes.  For the A operand of the value product the
@@ -548,14 +549,20 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(ReduceParams prm) {
 // ---------------------------------------------------------------------------------
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #ifndef PA_PREFIX_PREFETCH
 #define PA_PREFIX_PREFETCH 1  // 1: the prefix pass keeps the next tile's loads in flight
 #endif
-constexpr int kPrefixWaves = 4;
+#ifndef PA_PREFIX_WAVES
+#define PA_PREFIX_WAVES 8  // wave64s per prefix workgroup (4 or 8)
+#endif
+constexpr int kPrefixWaves = PA_PREFIX_WAVES;
+constexpr int kPrefixSlots = 4;  // wave states the LDS merge holds at once
 constexpr int kPrefixThreads = kPrefixWaves * kWave;
+static_assert(kPrefixWaves == kPrefixSlots || kPrefixWaves == 2 * kPrefixSlots, "prefix waves");
 constexpr int kTile = 16;  // tokens and queries per matrix-core tile
 
 // One lane's run of kN fp16 values of a V row (kN = 8: 16 bytes, kN = 4: 8 bytes).
@@ -577,9 +584,10 @@ template <int D, int BS>
 __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixParams prm) {
   static_assert(BS % kTile == 0 && (D == 64 || D == 128), "shape");
   constexpr int kTilesPerBlock = BS / kTile;
-  constexpr int kDq = D / 4;          // dims per lane in the score product
-  constexpr int kQLoads = kDq / 8;    // 16-byte loads of them
-  constexpr int kSteps = D / 16;      // score-product matrix-core steps over the dims
+  // score product: step c (of kQLoads) gives lane group j the dims
+  // [32c + 8j, 32c + 8j + 8) of its K row and query -- one 16-byte load each, and the
+  // four lane groups of a row read 64 contiguous bytes per load instruction
+  constexpr int kQLoads = D / 32;
   constexpr int kDv = D / 16;         // dims per lane per V row, also value-product tiles
 
   const int part = blockIdx.x;
@@ -608,18 +616,18 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
   const _Float16* v_head = static_cast<const _Float16*>(prm.value_cache) + static_cast<size_t>(head) * BS * D;
   const float scale_log2 = prm.scale * kLog2e;
 
-  __shared__ float s_m[kPrefixWaves][kTile];
-  __shared__ float s_l[kPrefixWaves][kTile];
-  __shared__ float s_o[kPrefixWaves][kTile][D + 1];  // +1: rows of one lane group hit distinct banks
+  __shared__ float s_m[kPrefixSlots][kTile];
+  __shared__ float s_l[kPrefixSlots][kTile];
+  __shared__ float s_o[kPrefixSlots][kTile][D + 1];  // +1: rows of one lane group hit distinct banks
 
   for (int q0 = 0; q0 < n_seqs; q0 += kTile) {
-    // B operand of the score product: query q0 + c16, dims [kDq*j, kDq*j + kDq)
+    // B operand of the score product: query q0 + c16, dims [32c + 8j, +8) per step c
     u32x4 qv[kQLoads];
     if (q0 + c16 < n_seqs) {
       const _Float16* qp = static_cast<const _Float16*>(prm.query) +
-                           (static_cast<size_t>(s0 + q0 + c16) * prm.num_heads + head) * D + kDq * j;
+                           (static_cast<size_t>(s0 + q0 + c16) * prm.num_heads + head) * D + 8 * j;
 #pragma unroll
-      for (int i = 0; i < kQLoads; ++i) qv[i] = load16(qp + 8 * i);
+      for (int i = 0; i < kQLoads; ++i) qv[i] = load16(qp + 32 * i);
     } else {
 #pragma unroll
       for (int i = 0; i < kQLoads; ++i) qv[i] = u32x4{0u, 0u, 0u, 0u};
@@ -636,12 +644,9 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
       // scores: sc[v] = <K row 4j+v, query c16>
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c = 0; c < kSteps; ++c) {
-        const u32x2 a = {kv[c / 2][2 * (c % 2)], kv[c / 2][2 * (c % 2) + 1]};
-        const u32x2 b = {qv[c / 2][2 * (c % 2)], qv[c / 2][2 * (c % 2) + 1]};
-        sc = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                   __builtin_bit_cast(f16x4, b), sc, 0, 0, 0);
-      }
+      for (int c = 0; c < kQLoads; ++c)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kv[c]),
+                                                    __builtin_bit_cast(f16x8, qv[c]), sc, 0, 0, 0);
       // online softmax of query c16 over the tile's 16 tokens (4 per lane group)
       float z[4];
 #pragma unroll
@@ -688,7 +693,7 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
                           ? table[(tile_begin + wave + idx * kPrefixWaves) / kTilesPerBlock]
                           : 0;
       const int n_here = min(n_mine - base, kWave);
-      // K row c16 (dims [kDq*j, kDq*j + kDq)) and V rows 4j+v (dims [kDv*c16, +kDv))
+      // K row c16 (dims [32c + 8j, +8) per step c) and V rows 4j+v (dims [kDv*c16, +kDv))
       // of the wave's i-th tile of this chunk
       auto load_tile = [&](int i, u32x4 (&kv)[kQLoads], HalfRun<kDv> (&vr)[4]) {
         const int tile = tile_begin + wave + (base + i) * kPrefixWaves;
@@ -696,7 +701,7 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
         const size_t off = static_cast<size_t>(phys) * block_stride +
                            static_cast<size_t>(tile % kTilesPerBlock) * kTile * D;
 #pragma unroll
-        for (int ii = 0; ii < kQLoads; ++ii) kv[ii] = load_kv16(k_head + off + c16 * D + kDq * j + 8 * ii);
+        for (int ii = 0; ii < kQLoads; ++ii) kv[ii] = load_kv16(k_head + off + c16 * D + 32 * ii + 8 * j);
 #pragma unroll
         for (int v = 0; v < 4; ++v) vr[v].load(v_head + off + (4 * j + v) * D + kDv * c16);
       };
@@ -724,16 +729,40 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
 #endif
     }
 
-    // merge the waves through LDS and leave one state per (sequence, head, partition)
-    if (j == 0) {
-      s_m[wave][c16] = m;
-      s_l[wave][c16] = l;
-    }
+    // Merge the waves and leave one state per (sequence, head, partition).  The LDS
+    // holds kPrefixSlots wave states: with more waves than slots, the upper waves
+    // park theirs first and the lower ones fold them in, in a fixed order.
+    auto park = [&](int slot) {
+      if (j == 0) {
+        s_m[slot][c16] = m;
+        s_l[slot][c16] = l;
+      }
 #pragma unroll
-    for (int dt = 0; dt < kDv; ++dt) {
+      for (int dt = 0; dt < kDv; ++dt) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s_o[wave][c16][kDv * (4 * j + v) + dt] = acc[dt][v];
+        for (int v = 0; v < 4; ++v) s_o[slot][c16][kDv * (4 * j + v) + dt] = acc[dt][v];
+      }
+    };
+    if constexpr (kPrefixWaves > kPrefixSlots) {
+      if (wave >= kPrefixSlots) park(wave - kPrefixSlots);
+      __syncthreads();
+      if (wave < kPrefixSlots) {
+        const float m_b = s_m[wave][c16];
+        const float mm = fmaxf(m, m_b);
+        const float fa = (m == -INFINITY) ? 0.0f : fast_exp2(m - mm);
+        const float fb = (m_b == -INFINITY) ? 0.0f : fast_exp2(m_b - mm);
+        l = l * fa + s_l[wave][c16] * fb;
+#pragma unroll
+        for (int dt = 0; dt < kDv; ++dt) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            acc[dt][v] = acc[dt][v] * fa + s_o[wave][c16][kDv * (4 * j + v) + dt] * fb;
+        }
+        m = mm;
+      }
+      __syncthreads();
     }
+    if (wave < kPrefixSlots) park(wave);
     __syncthreads();
     for (int e = threadIdx.x; e < kTile * D; e += kPrefixThreads) {
       const int g = e / D;
@@ -741,11 +770,11 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
       if (q0 + g >= n_seqs) break;  // e grows with g
       float mm = s_m[0][g];
 #pragma unroll
-      for (int w = 1; w < kPrefixWaves; ++w) mm = fmaxf(mm, s_m[w][g]);
+      for (int w = 1; w < kPrefixSlots; ++w) mm = fmaxf(mm, s_m[w][g]);
       float ll = 0.0f;
       float oo = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kPrefixWaves; ++w) {
+      for (int w = 0; w < kPrefixSlots; ++w) {
         const float f = (s_m[w][g] == -INFINITY) ? 0.0f : fast_exp2(s_m[w][g] - mm);
         ll = ll + s_l[w][g] * f;
         oo = oo + s_o[w][g][d] * f;

@@ -270,3 +270,17 @@ def test_long_context_full_batch():
     err = max_abs_err(got, want)
     print(f"long_context max-abs err {err:.3e}")
     assert err <= 2e-3, err
+
+
+def test_more_than_64_units_per_wave():
+    """Partitions long enough that a wave walks more than 64 units, so its block ids
+    are fetched in several chunks (block size 8: up to 9000 / 8 / 8 waves = 141 units
+    per wave in one partition)."""
+    b = workloads.make_static_batch("many_units", seed=31, num_seqs=2, num_heads=2, head_dim=128,
+                                    block_size=8, ctx_low=4000, ctx_high=9000,
+                                    dtype=np.float16)
+    db = DeviceBatch(b)
+    want = _oracle(b)
+    for part in (0, 8192, 4096):
+        got = db.decode(partition_size=part)
+        assert max_abs_err(got, want) <= 2e-3, part

@@ -161,3 +161,13 @@ def test_shared_prefix_full_batch_matches_oracle_and_pa_decode():
     assert err <= TOL, err
     plain = DeviceBatch(b).decode()
     assert max_abs_err(got, plain.astype(np.float64)) <= 2 * TOL
+
+
+def test_more_than_64_prefix_tiles_per_wave():
+    """One prefix partition of 9,000+ shared tokens: each of the 8 waves folds more than
+    64 tiles, so the tiles' block ids are fetched in several chunks."""
+    b = workloads.make_shared_prefix_batch("long_prefix", seed=47, group_sizes=[3], num_heads=2,
+                                           head_dim=64, block_size=16, prefix_blocks_low=570,
+                                           prefix_blocks_high=580, suffix_low=1, suffix_high=50)
+    got = run_shared(b, 0, 16384)
+    assert max_abs_err(got, _oracle(b)) <= TOL

@@ -35,10 +35,10 @@ METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 # raw values are in profiles/decode_partitions_llama7b_pmc.md.  Valid only for the
 # kernel source they were taken on.
 MEASURED_TRAFFIC = {
-    "kernel_source_sha256": "1bf82b9b32d5d6991f58e92c379e87944fb0923f0bd79d7af9c1b6a5aecd75af",
+    "kernel_source_sha256": "d92e3f0841f5a970f0cba4550ffb959a9d843120b414703ac14ca86649603e41",
     "seed": 2,
     "partition_tokens": 2048,
-    "read_bytes": 1934714857,
+    "read_bytes": 1934638082,
     "write_bytes": 786432,
 }
 KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -70,7 +70,9 @@ def parse():
     ap.add_argument("--no-mixes", dest="mixes", action="store_false",
                     help="skip the continuous-batching and shared-prefix step mixes")
     ap.add_argument("--no-extras", dest="extras", action="store_false",
-                    help="skip the long-context and shared-prefix batches")
+                    help="skip the long-context, shared-prefix, fp32, graph and swap sections")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the graph-replay section only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one pa_block_copy of a known size (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -97,6 +99,24 @@ def time_launches(fn, n, torch):
     stop.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / n
+
+
+def launch_spread(fn, n, torch):
+    """Per-launch ms of ``fn`` over n back-to-back launches, an event pair around each
+    on the current stream: 10th percentile, median and 90th percentile."""
+    stream = torch.cuda.current_stream()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in pairs])
+    p10, p50, p90 = np.percentile(t, [10, 50, 90])
+    return {"launches": n, "p10_ms": round(float(p10), 5), "median_ms": round(float(p50), 5),
+            "p90_ms": round(float(p90), 5)}
 
 
 def cpu_baseline(batch, budget_s):
@@ -192,6 +212,7 @@ def long_context_decode(torch, ops, metrics, args):
     n = max(10, args.steps // 4)
     ms = time_launches(decode, n, torch)
     ms_part = time_launches(partitions, n, torch)
+    spread = launch_spread(decode, n, torch)
     kv = metrics.decode_kv_bytes(b.context_lens, b.num_heads, b.head_dim, 2)
     del q, k, v, tables, ctx, out, ws
     torch.cuda.empty_cache()
@@ -206,6 +227,36 @@ def long_context_decode(torch, ops, metrics, args):
         "pct_of_hbm_peak": round(100.0 * metrics.gbps(kv, ms * 1e-3) / metrics.HBM_PEAK_GBPS, 2),
         "partition_pass_ms": round(ms_part, 5),
         "seq_steps_per_s": round(b.num_seqs / (ms * 1e-3), 1),
+        "decode_launch_ms": spread,
+    }
+
+
+def tiny_fp32_decode(torch, ops, metrics, args):
+    """pa_decode on the small fp32 batch (4 seqs x 4 heads x 64, block 16, 64-block
+    pool): launch-bound, shown for reference."""
+    from paged_kv_cache_414_amd import workloads
+
+    log(args, "tiny fp32 batch")
+    b = workloads.tiny_fp32(seed=1, poison=False)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    q, k, v = dev(b.q), dev(b.k_pool), dev(b.v_pool)
+    tables, ctx = dev(b.block_tables), dev(b.context_lens)
+    out = torch.empty_like(q)
+    ws = ops.workspace_for(q, k, b.max_context_len, 0)
+
+    def decode():
+        ops.pa_decode(out, q, k, v, tables, ctx, b.scale, b.max_context_len, 0, ws)
+
+    for _ in range(20):
+        decode()
+    n = max(50, args.steps)
+    ms = time_launches(decode, n, torch)
+    return {
+        "num_seqs": b.num_seqs, "num_heads": b.num_heads, "head_dim": b.head_dim,
+        "block_size": b.block_size, "dtype": "f32", "sum_context": int(b.context_lens.sum()),
+        "decode_ms": round(ms, 5),
+        "seq_steps_per_s": round(b.num_seqs / (ms * 1e-3), 1),
+        "decode_launch_ms": launch_spread(decode, n, torch),
     }
 
 
@@ -408,6 +459,7 @@ def main():
         partitions_only()
     ms_part = time_launches(partitions_only, args.steps, torch)
     ms_decode = time_launches(decode_only, args.steps, torch)
+    decode_spread = launch_spread(decode_only, args.steps, torch)
 
     kv = metrics.decode_kv_bytes(ctx, h_count, d, batch.q.itemsize)
     value = metrics.gbps(kv, ms_step * 1e-3)
@@ -438,6 +490,7 @@ def main():
         "seq_steps_per_s": round(s_count / (ms_step * 1e-3), 1),
         "decode_ms": round(ms_decode, 5),
         "decode_kv_gbps": round(metrics.gbps(kv, ms_decode * 1e-3), 2),
+        "decode_launch_ms": decode_spread,
         "kv_bytes_per_step": kv,
         "roofline": {
             "kernel": "decode_partitions_kernel<f16, 128, 16>",
@@ -453,8 +506,10 @@ def main():
     }
     if args.extras:
         record["long_context"] = long_context_decode(torch, ops, metrics, args)
+        record["tiny_fp32"] = tiny_fp32_decode(torch, ops, metrics, args)
         record["shared_prefix_decode"] = shared_prefix_decode(torch, ops, metrics, args)
-        record["graph_step"] = graph_step(torch, ops, metrics, args)
+        if args.graph:
+            record["graph_step"] = graph_step(torch, ops, metrics, args)
         record["block_swap"] = swap_throughput(torch, ops, args)
     if args.mixes:
         record["step_mixes"] = {

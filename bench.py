@@ -159,27 +159,36 @@ def cpu_baseline(batch, budget_s):
 
 
 def run_mix(cls_name, seed, torch, args, **kw):
-    """One full run of a step mix: wall-clock seq-steps/s (host block manager, the
-    small per-step H2D copies and the launches included; synthetic inputs staged in
-    HBM beforehand) and the last step's decode re-timed alone."""
+    """One full run of a step mix, each step one call of the native decode-step
+    executor: wall-clock seq-steps/s (host block manager, the per-step H2D copy and
+    the launches included; synthetic inputs staged in HBM beforehand) and the last
+    step's decode re-timed alone.  The same mix driven step by step from Python (the
+    same native block manager and kernels, one binding call per operation) is timed
+    beside it."""
     from paged_kv_cache_414_amd import metrics, steps
 
+    def wall_run(native):
+        mix = getattr(steps, cls_name)(seed=seed, native=native, **kw)
+        mix.prepare()  # every step's synthetic inputs drawn and placed in HBM
+        t0 = time.perf_counter()
+        rows = 0
+        for k in range(mix.steps):
+            rows += mix.run_step(k)
+        torch.cuda.synchronize()
+        return mix, rows, time.perf_counter() - t0
+
     log(args, f"step mix {cls_name} {kw}")
-    mix = getattr(steps, cls_name)(seed=seed, **kw)
-    mix.prepare()  # every step's synthetic inputs drawn and placed in HBM
-    t0 = time.perf_counter()
-    rows = 0
-    for k in range(mix.steps):
-        ctx = mix.run_step(k)
-        rows += len(ctx)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    mix, rows, wall = wall_run(native=True)
     ms = time_launches(mix.decode_again, 50, torch)
+    ctx = mix.last_context_lens()
     kv = mix.kv_bytes(ctx)
+    _, rows_py, wall_py = wall_run(native=False)
     return {
         "steps": mix.steps,
         "seq_steps_per_s_wall": round(rows / wall, 1),
         "wall_s": round(wall, 4),
+        "driver": "native executor, one pa_step_run per step",
+        "python_driver_seq_steps_per_s_wall": round(rows_py / wall_py, 1),
         "copy_on_write_pairs": mix.copies_total,
         "last_step_decode_ms": round(ms, 5),
         "last_step_decode_kv_gbps": round(metrics.gbps(kv, ms * 1e-3), 1),

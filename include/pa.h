@@ -39,9 +39,10 @@
  *      slot_mapping          int32 [num_tokens]; slot = block * block_size + offset.
  *                            A negative slot means "skip this row".
  *      block_pairs           int32 [num_pairs, 2] = (source block, destination block).
- *  * Supported shapes: head_dim in {64, 128}; block_size in {8, 16, 32}
- *    (pa_decode_shared_prefix: fp16, block_size 16 or 32); other values return
- *    PA_ERR_UNSUPPORTED.  K/V heads equal query heads.
+ *  * Supported shapes: head_dim in {64, 80, 96, 128, 256}; block_size in {8, 16,
+ *    32, 64, 128, 256} (pa_decode_shared_prefix: fp16, head_dim 64 or 128,
+ *    block_size 16 to 256); other values return PA_ERR_UNSUPPORTED.  K/V heads
+ *    equal query heads.
  *  * Errors: argument checks run on the host before anything is enqueued and return
  *    a status; nothing aborts and no C++ exception crosses the ABI.  A failed launch
  *    returns PA_ERR_HIP.  The text of the last error of the calling thread is
@@ -269,8 +270,8 @@ pa_status pa_swap_blocks(void* dst_key, void* dst_value, const void* src_key,
  *   max_suffix_len host: >= every context_lens[s] - prefix_lens[s].
  * Both are <= max_blocks_per_seq * block_size, and every context_lens[s] is too.
  * Groups of any size are accepted; a group's prefix is read once per 16 members.
- * Built for PA_F16, head_dim in {64, 128} and block_size in {16, 32}; other values
- * return PA_ERR_UNSUPPORTED.  partition_size applies to the tokens after the prefix
+ * Built for PA_F16, head_dim in {64, 128} and block_size in {16, 32, 64, 128, 256};
+ * other values return PA_ERR_UNSUPPORTED.  partition_size applies to the tokens after the prefix
  * (as in pa_decode, sized by max_suffix_len); prefix_partition_size is the number
  * of prefix tokens one workgroup reads (0 = library choice, else a positive
  * multiple of max(16, block_size)).  The contents above are caller preconditions

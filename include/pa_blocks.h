@@ -47,6 +47,11 @@ typedef struct pa_block_manager pa_block_manager;
 pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size, uint64_t seed);
 void pa_bm_destroy(pa_block_manager* bm);
 
+/* The pool the manager was created over: its blocks, and token slots per block
+ * (-1 for a NULL manager). */
+int32_t pa_bm_num_blocks(const pa_block_manager* bm);
+int32_t pa_bm_block_size(const pa_block_manager* bm);
+
 /* Free blocks; 1 if ceil(num_tokens / block_size) blocks are free, else 0. */
 int32_t pa_bm_num_free(const pa_block_manager* bm);
 int32_t pa_bm_can_allocate(const pa_block_manager* bm, int32_t num_tokens);

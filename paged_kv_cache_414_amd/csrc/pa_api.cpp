@@ -34,6 +34,17 @@ pa_status clear_error() {
   return PA_OK;
 }
 
+pa_status check_dtype_shape(pa_dtype dtype, int32_t head_dim, int32_t block_size) {
+  if (dtype != PA_F32 && dtype != PA_F16)
+    return set_error(PA_ERR_UNSUPPORTED, "dtype %d is not PA_F32 or PA_F16", (int)dtype);
+  if (head_dim != 64 && head_dim != 80 && head_dim != 96 && head_dim != 128 && head_dim != 256)
+    return set_error(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 80, 96, 128, 256)", head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128 &&
+      block_size != 256)
+    return set_error(PA_ERR_UNSUPPORTED, "block_size %d is not built (8, 16, 32, 64, 128, 256)", block_size);
+  return PA_OK;
+}
+
 }  // namespace pa
 
 namespace {
@@ -66,15 +77,7 @@ size_t elem_bytes(pa_dtype dt) { return dt == PA_F16 ? 2 : 4; }
 
 size_t ws_align(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
-pa_status check_dtype_shape(pa_dtype dtype, int32_t head_dim, int32_t block_size) {
-  if (dtype != PA_F32 && dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "dtype %d is not PA_F32 or PA_F16", (int)dtype);
-  if (head_dim != 64 && head_dim != 80 && head_dim != 96 && head_dim != 128 && head_dim != 256)
-    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 80, 96, 128, 256)", head_dim);
-  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128 &&
-      block_size != 256)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not built (8, 16, 32, 64, 128, 256)", block_size);
-  return PA_OK;
-}
+using pa::check_dtype_shape;
 
 int32_t round_up(int64_t x, int32_t m) { return static_cast<int32_t>(((x + m - 1) / m) * m); }
 

@@ -111,6 +111,10 @@ pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size, uint64_t 
 
 void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
 
+int32_t pa_bm_num_blocks(const pa_block_manager* bm) { return bm ? bm->num_blocks : -1; }
+
+int32_t pa_bm_block_size(const pa_block_manager* bm) { return bm ? bm->block_size : -1; }
+
 int32_t pa_bm_num_free(const pa_block_manager* bm) {
   return bm ? static_cast<int32_t>(bm->free_list.size()) : -1;
 }

@@ -96,6 +96,9 @@ hipError_t launch_decode_prefix(const PrefixParams& prm, int head_dim, int block
                                 hipStream_t stream);
 hipError_t launch_cache_append(const AppendParams& prm, hipStream_t stream);
 hipError_t launch_block_copy(const CopyParams& prm, hipStream_t stream);
+// bytes / 16 words from `src` (device-visible pinned host memory) to `dst` (device);
+// bytes a multiple of 16, both 16-byte aligned.
+hipError_t launch_stage_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
 }  // namespace pa
 

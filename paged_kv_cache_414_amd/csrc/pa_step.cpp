@@ -1,0 +1,377 @@
+// Decode-step executor: one host call per decode step (block manager, staging of
+// the step's small arrays in pinned memory, one host-to-device copy, the kernels of
+// pa.h).  The contract is documented in include/pa_step.h.
+
+#include "pa_step.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "pa_launch.h"
+#include "pa_status.h"
+
+namespace {
+
+constexpr int64_t kAlign = 4;  // int32 elements: every staged array starts 16-byte aligned
+
+int64_t aligned(int64_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+pa_status hip_fail(hipError_t err, const char* what) {
+  return pa::set_error(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+template <typename T>
+bool all_distinct(const T* ids, int32_t n, std::vector<T>& scratch) {
+  scratch.assign(ids, ids + n);
+  std::sort(scratch.begin(), scratch.end());
+  return std::adjacent_find(scratch.begin(), scratch.end()) == scratch.end();
+}
+
+}  // namespace
+
+struct pa_step_engine {
+  pa_block_manager* bm = nullptr;
+  pa_step_config cfg{};
+  int32_t block_size = 0;
+  int32_t num_blocks = 0;
+  void* key_cache = nullptr;
+  void* value_cache = nullptr;
+  int device = 0;
+
+  // Staging layout, int32 offsets; the same in the pinned and the device buffer.
+  int64_t off_pairs = 0, off_slots = 0, off_tables = 0, off_ctx = 0, off_starts = 0,
+          off_prefix = 0, off_admit = 0, capacity = 0;
+  int32_t* host[2] = {nullptr, nullptr};       // pinned, written by the host
+  const void* host_dev[2] = {nullptr, nullptr};  // the same buffers as the device sees them
+  hipEvent_t copied[2] = {nullptr, nullptr};
+  bool in_flight[2] = {false, false};
+  hipEvent_t step_done = nullptr;  // after the last kernel of the last step
+  bool step_pending = false;
+  int turn = 0;
+  int32_t* dev = nullptr;
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+
+  std::vector<int32_t> positions;
+  std::vector<int64_t> id_scratch;
+
+  // the last step, for pa_step_last
+  bool has_last = false;
+  int last_turn = 0;
+  int32_t last_n = 0;
+  int32_t last_groups = 0;
+  pa_step_result last{};
+
+  ~pa_step_engine() {
+    if (step_done) {
+      if (step_pending) (void)hipEventSynchronize(step_done);
+      (void)hipEventDestroy(step_done);
+    }
+    for (int i = 0; i < 2; ++i) {
+      if (copied[i]) {
+        if (in_flight[i]) (void)hipEventSynchronize(copied[i]);
+        (void)hipEventDestroy(copied[i]);
+      }
+      if (host[i]) (void)hipHostFree(host[i]);
+    }
+    if (dev) (void)hipFree(dev);
+    if (workspace) (void)hipFree(workspace);
+  }
+
+  const int32_t* dev_at(int64_t off) const { return dev + off; }
+  int32_t* dev_at(int64_t off) { return dev + off; }
+};
+
+extern "C" {
+
+pa_step_engine* pa_step_create(pa_block_manager* bm, const pa_step_config* config, void* key_cache,
+                               void* value_cache) {
+  if (!bm || !config || !key_cache || !value_cache) {
+    pa::set_error(PA_ERR_NULL, "manager, config and both pools must not be NULL");
+    return nullptr;
+  }
+  const pa_step_config& c = *config;
+  const int32_t bs = pa_bm_block_size(bm);
+  if (pa::check_dtype_shape(c.dtype, c.head_dim, bs) != PA_OK) return nullptr;
+  if (c.num_heads <= 0 || c.max_seqs <= 0 || c.max_blocks_per_seq <= 0 || c.max_admit_tokens < 0 ||
+      c.max_groups < 0) {
+    pa::set_error(PA_ERR_INVALID_ARG,
+                  "num_heads %d, max_seqs %d, max_blocks_per_seq %d must be positive; max_admit_tokens %d "
+                  "and max_groups %d non-negative",
+                  c.num_heads, c.max_seqs, c.max_blocks_per_seq, c.max_admit_tokens, c.max_groups);
+    return nullptr;
+  }
+  if (static_cast<int64_t>(c.max_blocks_per_seq) * bs > INT32_MAX) {
+    pa::set_error(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size exceeds the int32 range");
+    return nullptr;
+  }
+  pa_step_engine* e = new (std::nothrow) pa_step_engine;
+  if (!e) {
+    pa::set_error(PA_ERR_INVALID_ARG, "out of host memory");
+    return nullptr;
+  }
+  e->bm = bm;
+  e->cfg = c;
+  e->block_size = bs;
+  e->num_blocks = pa_bm_num_blocks(bm);
+  e->key_cache = key_cache;
+  e->value_cache = value_cache;
+
+  const int64_t s = c.max_seqs;
+  int64_t at = 0;
+  e->off_pairs = at;  at += aligned(2 * s);
+  e->off_slots = at;  at += aligned(s);
+  e->off_tables = at; at += aligned(s * c.max_blocks_per_seq);
+  e->off_ctx = at;    at += aligned(s);
+  e->off_starts = at; at += c.max_groups > 0 ? aligned(c.max_groups + 1) : 0;
+  e->off_prefix = at; at += c.max_groups > 0 ? aligned(s) : 0;
+  e->off_admit = at;  at += aligned(c.max_admit_tokens);
+  e->capacity = at;
+  e->positions.resize(s);
+
+  hipError_t err = hipGetDevice(&e->device);
+  const size_t bytes = static_cast<size_t>(e->capacity) * sizeof(int32_t);
+  for (int i = 0; i < 2 && err == hipSuccess; ++i) {
+    // coherent: the staging kernel reads what the host wrote just before the launch
+    err = hipHostMalloc(reinterpret_cast<void**>(&e->host[i]), bytes,
+                        hipHostMallocMapped | hipHostMallocCoherent);
+    void* mapped = nullptr;
+    if (err == hipSuccess) err = hipHostGetDevicePointer(&mapped, e->host[i], 0);
+    e->host_dev[i] = mapped;
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&e->copied[i], hipEventDisableTiming);
+  }
+  if (err == hipSuccess) err = hipEventCreateWithFlags(&e->step_done, hipEventDisableTiming);
+  if (err == hipSuccess) err = hipMalloc(reinterpret_cast<void**>(&e->dev), bytes);
+  if (err != hipSuccess) {
+    hip_fail(err, "pa_step_create: allocation");
+    delete e;
+    return nullptr;
+  }
+  pa::clear_error();
+  return e;
+}
+
+void pa_step_destroy(pa_step_engine* engine) { delete engine; }
+
+pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa_step_result* result) {
+  if (!e || !a) return pa::set_error(PA_ERR_NULL, "engine and args must not be NULL");
+  const pa_step_config& c = e->cfg;
+  const int32_t n = a->num_seqs;
+  const int32_t bs = e->block_size;
+  const int32_t mb = c.max_blocks_per_seq;
+
+  // ---- argument checks: nothing changes before all of them pass ----
+  if (n < 1 || n > c.max_seqs)
+    return pa::set_error(PA_ERR_INVALID_ARG, "num_seqs %d outside [1, %d]", n, c.max_seqs);
+  if (!a->seq_ids || !a->query || !a->new_key || !a->new_value || !a->out)
+    return pa::set_error(PA_ERR_NULL, "seq_ids, query, new_key, new_value and out must not be NULL");
+  if (a->num_groups < 0 || a->num_groups > c.max_groups)
+    return pa::set_error(PA_ERR_INVALID_ARG, "num_groups %d outside [0, %d]", a->num_groups, c.max_groups);
+  const int32_t g_count = a->num_groups;
+  if (g_count > 0) {
+    if (!a->group_starts) return pa::set_error(PA_ERR_NULL, "group_starts must not be NULL");
+    if (a->group_starts[0] != 0 || a->group_starts[g_count] != n)
+      return pa::set_error(PA_ERR_INVALID_ARG, "group_starts must run from 0 to num_seqs %d", n);
+    for (int32_t g = 0; g < g_count; ++g) {
+      if (a->group_starts[g + 1] < a->group_starts[g])
+        return pa::set_error(PA_ERR_INVALID_ARG, "group_starts must be non-decreasing");
+    }
+  }
+  if (a->num_finished < 0 || a->num_admit < 0)
+    return pa::set_error(PA_ERR_INVALID_ARG, "num_finished %d and num_admit %d must be >= 0", a->num_finished,
+                         a->num_admit);
+  if (a->num_finished > 0 && !a->finished_ids) return pa::set_error(PA_ERR_NULL, "finished_ids is NULL");
+  if (a->num_admit > 0 && (!a->admit_ids || !a->admit_lens))
+    return pa::set_error(PA_ERR_NULL, "admit_ids and admit_lens must not be NULL");
+  if (!all_distinct(a->seq_ids, n, e->id_scratch))
+    return pa::set_error(PA_ERR_INVALID_ARG, "a running sequence is listed twice");
+  if (!all_distinct(a->finished_ids, a->num_finished, e->id_scratch))
+    return pa::set_error(PA_ERR_INVALID_ARG, "a finished sequence is listed twice");
+  if (!all_distinct(a->admit_ids, a->num_admit, e->id_scratch))
+    return pa::set_error(PA_ERR_INVALID_ARG, "a request id is listed twice");
+  int64_t requested = 0;
+  for (int32_t i = 0; i < a->num_admit; ++i) {
+    if (a->admit_lens[i] < 0) return pa::set_error(PA_ERR_INVALID_ARG, "admit_lens[%d] is negative", i);
+    if (pa_bm_num_seq_blocks(e->bm, a->admit_ids[i]) >= 0)
+      return pa::set_error(PA_ERR_INVALID_ARG, "request id %lld is a known sequence", (long long)a->admit_ids[i]);
+    requested += a->admit_lens[i];
+  }
+  if (requested > c.max_admit_tokens)
+    return pa::set_error(PA_ERR_INVALID_ARG, "%lld prompt tokens requested, the executor stages %d",
+                         (long long)requested, c.max_admit_tokens);
+  if (requested > 0 && (!a->prompt_key || !a->prompt_value))
+    return pa::set_error(PA_ERR_NULL, "prompt_key and prompt_value must not be NULL");
+  for (int32_t i = 0; i < a->num_finished; ++i) {
+    if (pa_bm_num_seq_blocks(e->bm, a->finished_ids[i]) < 0)
+      return pa::set_error(PA_ERR_INVALID_ARG, "finished sequence %lld is unknown", (long long)a->finished_ids[i]);
+  }
+  int current_device = 0;
+  hipError_t err = hipGetDevice(&current_device);
+  if (err != hipSuccess) return hip_fail(err, "pa_step_run: hipGetDevice");
+  if (current_device != e->device)
+    return pa::set_error(PA_ERR_INVALID_ARG, "the executor lives on device %d, device %d is current", e->device,
+                         current_device);
+
+  // ---- this step's pinned buffer: its last copy (two steps ago) must be done ----
+  const int t = e->turn;
+  if (e->in_flight[t]) {
+    err = hipEventSynchronize(e->copied[t]);
+    if (err != hipSuccess) return hip_fail(err, "pa_step_run: waiting for the staging copy");
+    e->in_flight[t] = false;
+  }
+  int32_t* h = e->host[t];
+  int32_t* ctx = h + e->off_ctx;
+
+  // Context lengths before the step bound the table width; also rejects unknown ids.
+  pa_status st = pa_bm_context_lens(e->bm, a->seq_ids, n, ctx);
+  if (st != PA_OK) return st;
+  for (int32_t i = 0; i < n; ++i) {
+    if (static_cast<int64_t>(ctx[i]) + 1 > static_cast<int64_t>(mb) * bs)
+      return pa::set_error(PA_ERR_INVALID_ARG, "sequence %lld would exceed %d blocks", (long long)a->seq_ids[i],
+                           mb);
+  }
+
+  // ---- 1. slots of the new tokens (all or nothing) ----
+  int32_t copies = 0;
+  st = pa_bm_append_slots(e->bm, a->seq_ids, n, h + e->off_slots, e->positions.data(), h + e->off_pairs, &copies);
+  if (st != PA_OK) return st;
+
+  // ---- 2. tables, lengths, shared prefixes ----
+  pa_bm_block_tables(e->bm, a->seq_ids, n, mb, 0, h + e->off_tables);
+  int32_t max_ctx = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    ctx[i] = e->positions[i] + 1;
+    max_ctx = std::max(max_ctx, ctx[i]);
+  }
+  int32_t max_prefix = 0, max_suffix = 0;
+  if (g_count > 0) {
+    int32_t* starts = h + e->off_starts;
+    int32_t* prefix = h + e->off_prefix;
+    for (int32_t g = 0; g <= g_count; ++g) starts[g] = a->group_starts[g];
+    for (int32_t g = 0; g < g_count; ++g) {
+      const int32_t r0 = starts[g], r1 = starts[g + 1];
+      if (r1 == r0) continue;
+      const int32_t shared = pa_bm_shared_prefix_blocks(e->bm, a->seq_ids + r0, r1 - r0);
+      for (int32_t r = r0; r < r1; ++r) {
+        prefix[r] = shared * bs;
+        max_prefix = std::max(max_prefix, prefix[r]);
+        max_suffix = std::max(max_suffix, ctx[r] - prefix[r]);
+      }
+    }
+  }
+
+  // ---- 3. retire, then admit while the blocks fit ----
+  for (int32_t i = 0; i < a->num_finished; ++i) pa_bm_free(e->bm, a->finished_ids[i]);
+  int32_t admitted = 0;
+  int64_t admitted_tokens = 0;
+  {
+    int64_t free_blocks = pa_bm_num_free(e->bm);
+    while (admitted < a->num_admit) {
+      const int64_t need = (static_cast<int64_t>(a->admit_lens[admitted]) + bs - 1) / bs;
+      if (need > free_blocks) break;
+      free_blocks -= need;
+      admitted_tokens += a->admit_lens[admitted];
+      ++admitted;
+    }
+    if (admitted > 0) pa_bm_add_sequences(e->bm, a->admit_ids, a->admit_lens, admitted, h + e->off_admit);
+  }
+
+  // ---- 4. one copy of the staged arrays, by a kernel on the step's stream ----
+  const int64_t used = aligned(admitted_tokens > 0 ? e->off_admit + admitted_tokens : e->off_admit);
+  err = pa::launch_stage_copy(e->host_dev[t], e->dev, used * static_cast<int64_t>(sizeof(int32_t)),
+                              static_cast<hipStream_t>(stream));
+  if (err == hipSuccess) err = hipEventRecord(e->copied[t], static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "pa_step_run: staging copy");
+  e->in_flight[t] = true;
+  e->turn ^= 1;
+
+  // ---- 5. kernels, in stream order ----
+  const int32_t H = c.num_heads, D = c.head_dim, NB = e->num_blocks;
+  const size_t need_ws =
+      g_count > 0 ? pa_decode_shared_prefix_workspace_bytes(n, H, D, bs, g_count, max_prefix, max_suffix, 0, 0)
+                  : pa_decode_workspace_bytes(n, H, D, bs, max_ctx, 0);
+  if (need_ws > e->workspace_bytes) {
+    // only earlier steps used the old workspace: wait for the last of them
+    if (e->step_pending) err = hipEventSynchronize(e->step_done);
+    e->step_pending = false;
+    if (err == hipSuccess && e->workspace) err = hipFree(e->workspace);
+    e->workspace = nullptr;
+    e->workspace_bytes = 0;
+    const size_t grown = need_ws + need_ws / 4;
+    if (err == hipSuccess) err = hipMalloc(&e->workspace, grown);
+    if (err != hipSuccess) return hip_fail(err, "pa_step_run: decode workspace");
+    e->workspace_bytes = grown;
+  }
+  if (copies > 0) {
+    st = pa_block_copy(e->key_cache, e->value_cache, e->dev_at(e->off_pairs), copies, H, D, bs, NB, c.dtype,
+                       stream);
+    if (st != PA_OK) return st;
+  }
+  st = pa_cache_append(e->key_cache, e->value_cache, a->new_key, a->new_value, e->dev_at(e->off_slots), n, H, D,
+                       bs, NB, c.dtype, stream);
+  if (st != PA_OK) return st;
+  if (g_count > 0) {
+    st = pa_decode_shared_prefix(a->out, a->query, e->key_cache, e->value_cache, e->dev_at(e->off_tables),
+                                 e->dev_at(e->off_ctx), e->dev_at(e->off_starts), e->dev_at(e->off_prefix), n, H,
+                                 D, bs, NB, mb, g_count, max_prefix, max_suffix, a->scale, c.dtype, 0, 0,
+                                 e->workspace, e->workspace_bytes, stream);
+  } else {
+    st = pa_decode(a->out, a->query, e->key_cache, e->value_cache, e->dev_at(e->off_tables), e->dev_at(e->off_ctx),
+                   n, H, D, bs, NB, mb, max_ctx, a->scale, c.dtype, 0, e->workspace, e->workspace_bytes, stream);
+  }
+  if (st != PA_OK) return st;
+  if (admitted_tokens > 0) {
+    st = pa_cache_append(e->key_cache, e->value_cache, a->prompt_key, a->prompt_value, e->dev_at(e->off_admit),
+                         static_cast<int32_t>(admitted_tokens), H, D, bs, NB, c.dtype, stream);
+    if (st != PA_OK) return st;
+  }
+  err = hipEventRecord(e->step_done, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "pa_step_run: recording the step's end");
+  e->step_pending = true;
+
+  pa_step_result r{};
+  r.num_copies = copies;
+  r.num_admitted = admitted;
+  r.admitted_tokens = static_cast<int32_t>(admitted_tokens);
+  r.max_context_len = max_ctx;
+  r.max_prefix_len = max_prefix;
+  r.max_suffix_len = max_suffix;
+  e->last = r;
+  e->has_last = true;
+  e->last_turn = t;
+  e->last_n = n;
+  e->last_groups = g_count;
+  if (result) *result = r;
+  return pa::clear_error();
+}
+
+pa_status pa_step_last(const pa_step_engine* e, pa_step_view* v) {
+  if (!e || !v) return pa::set_error(PA_ERR_NULL, "engine and view must not be NULL");
+  if (!e->has_last) return pa::set_error(PA_ERR_INVALID_ARG, "no step has run on this executor");
+  const int32_t* h = e->host[e->last_turn];
+  const bool grouped = e->last_groups > 0;
+  v->num_seqs = e->last_n;
+  v->num_groups = e->last_groups;
+  v->result = e->last;
+  v->slots = h + e->off_slots;
+  v->positions = e->positions.data();
+  v->copy_pairs = h + e->off_pairs;
+  v->block_tables = h + e->off_tables;
+  v->context_lens = h + e->off_ctx;
+  v->group_starts = grouped ? h + e->off_starts : nullptr;
+  v->prefix_lens = grouped ? h + e->off_prefix : nullptr;
+  v->admit_slots = h + e->off_admit;
+  v->dev_block_tables = e->dev_at(e->off_tables);
+  v->dev_context_lens = e->dev_at(e->off_ctx);
+  v->dev_group_starts = grouped ? e->dev_at(e->off_starts) : nullptr;
+  v->dev_prefix_lens = grouped ? e->dev_at(e->off_prefix) : nullptr;
+  v->workspace = e->workspace;
+  v->workspace_bytes = e->workspace_bytes;
+  return pa::clear_error();
+}
+
+}  // extern "C"

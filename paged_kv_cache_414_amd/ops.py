@@ -45,6 +45,8 @@ SIGNATURES = {
     # host block manager (include/pa_blocks.h)
     "pa_bm_create": (_vp, [_i32, _i32, ctypes.c_uint64]),
     "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_num_blocks": (_i32, [_vp]),
+    "pa_bm_block_size": (_i32, [_vp]),
     "pa_bm_num_free": (_i32, [_vp]),
     "pa_bm_can_allocate": (_i32, [_vp, _i32]),
     "pa_bm_ref_counts": (_i32, [_vp, _vp]),
@@ -60,6 +62,11 @@ SIGNATURES = {
     "pa_bm_seq_blocks": (_i32, [_vp, ctypes.c_int64, _vp, _i32]),
     "pa_decode_shared_prefix": (_i32, [_vp] * 8 + [_i32] * 9 + [_f32, _i32, _i32, _i32, _vp,
                                                                 _sz, _vp]),
+    # decode-step executor (include/pa_step.h); structs are passed by pointer
+    "pa_step_create": (_vp, [_vp, _vp, _vp, _vp]),
+    "pa_step_destroy": (None, [_vp]),
+    "pa_step_run": (_i32, [_vp, _vp, _vp, _vp]),
+    "pa_step_last": (_i32, [_vp, _vp]),
 }
 
 

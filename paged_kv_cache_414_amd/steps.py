@@ -123,7 +123,8 @@ class StepMix:
 
     def __init__(self, spec: workloads.StepMixSpec, draws: workloads.StepDraws,
                  steps: int, max_blocks_per_seq: int, device="cuda",
-                 keep_records=False, staging_extra: int = 0):
+                 keep_records=False, staging_extra: int = 0, native=False,
+                 max_admit_tokens: int = 0, max_groups: int = 0):
         self.spec = spec
         self.draws = draws
         self.steps = int(steps)
@@ -151,6 +152,14 @@ class StepMix:
         per_step = 4 * s + s * self.mb + (s + 1) + s + 8 * Staging.ALIGN
         self.staging = Staging(per_step + int(staging_extra), device)
         self._positions = np.empty(s, dtype=np.int32)
+        self._last_ctx = None
+        # native: each step is one call of the decode-step executor (pa_step.h)
+        self.engine = None
+        if native:
+            from . import engine
+            self.engine = engine.StepEngine(self.manager, self.k_cache, self.v_cache, s, self.mb,
+                                            max_admit_tokens=max_admit_tokens,
+                                            max_groups=max_groups)
 
     # -- inputs ---------------------------------------------------------------------
     def _draw_inputs(self, k: int) -> StepInputs:
@@ -206,7 +215,10 @@ class StepMix:
         returns a callable that enqueues this step's work after the decode, or None."""
         return None
 
-    def step(self, k_step: int):
+    def step(self, k_step: int) -> int:
+        """Run step ``k_step``; returns the number of sequences decoded."""
+        if self.engine is not None:
+            return self._native_step(k_step)
         st = self.staging
         st.begin()
         n = len(self.lanes)
@@ -242,7 +254,51 @@ class StepMix:
             rec.new_k, rec.new_v, rec.q = inp.new_k, inp.new_v, inp.q
             self._finish_record(rec)
             self.records.append(rec)
-        return ctx
+        self._last_ctx = ctx
+        return n
+
+    def last_context_lens(self) -> np.ndarray:
+        """Context lengths of the last step's sequences (the new token counted)."""
+        if self.engine is not None:
+            return self.engine.last()["context_lens"]
+        return np.array(self._last_ctx)
+
+    # -- one step through the native executor -----------------------------------------
+    def _native_requests(self, k_step: int, inp: StepInputs) -> dict:
+        """Subclass hook: finished sequences and admission requests of the step."""
+        return {}
+
+    def _native_groups(self):
+        """Subclass hook: group_starts of a shared-prefix decode, or None."""
+        return None
+
+    def _native_step(self, k_step: int) -> int:
+        inp = self.inputs(k_step)
+        nk_d, nv_d, q_d = inp.dev[:3] if inp.dev else (self.to_dev(inp.new_k),
+                                                        self.to_dev(inp.new_v),
+                                                        self.to_dev(inp.q))
+        req = self._native_requests(k_step, inp)
+        groups = self._native_groups()
+        n = len(self.lanes)
+        res = self.engine.run(self.lanes, q_d, nk_d, nv_d, self.out, self.scale,
+                              group_starts=groups, **req)
+        self.copies_total += res.num_copies
+        if "admit_ids" in req:
+            if res.num_admitted != len(req["admit_ids"]):
+                raise blocks.OutOfBlocks(f"{res.num_admitted} of {len(req['admit_ids'])} "
+                                         "requests admitted")
+            self.lanes[inp.finishing] = req["admit_ids"]
+        if self.keep:
+            v = self.engine.last()
+            rec = StepRecord(k_step, v["copy_pairs"], v["slots"], inp.new_k, inp.new_v,
+                             v["positions"], v["block_tables"], v["context_lens"], inp.q)
+            if v["admit_slots"].size:
+                rec.post_slots, rec.post_k, rec.post_v = v["admit_slots"], inp.prompt_k, inp.prompt_v
+            if groups is not None:
+                self.last_prefix = (v["group_starts"], v["prefix_lens"])
+            self.records.append(rec)
+        self.last_decode = lambda: self.engine.decode_again(q_d, self.out, self.scale)
+        return n
 
     def _finish_record(self, rec: StepRecord) -> None:
         pass
@@ -273,13 +329,14 @@ class ContinuousBatching(StepMix):
     """64 running sequences, 13 replaced after every step (see module docstring)."""
 
     def __init__(self, seed: int, steps: int | None = None, device="cuda",
-                 keep_records=False):
+                 keep_records=False, native=False):
         spec = workloads.CONTINUOUS_BATCHING
         draws = workloads.ContinuousBatchingDraws(spec, seed)
         steps = steps or spec.steps
         mb = -(-(draws.prompt_high + steps) // spec.block_size)
         prompt_room = draws.finish_count * draws.prompt_high + Staging.ALIGN
-        super().__init__(spec, draws, steps, mb, device, keep_records, staging_extra=prompt_room)
+        super().__init__(spec, draws, steps, mb, device, keep_records, staging_extra=prompt_room,
+                         native=native, max_admit_tokens=prompt_room)
         lens = draws.initial_prompt_lens()
         k, v = draws.prompt_kv(-1, lens)
         slots = np.empty(int(lens.sum()) + 1, dtype=np.int32)
@@ -319,6 +376,14 @@ class ContinuousBatching(StepMix):
         inp = self.inputs(rec.step)
         rec.post_slots, rec.post_k, rec.post_v = self._post, inp.prompt_k, inp.prompt_v
 
+    def _native_requests(self, k_step: int, inp: StepInputs) -> dict:
+        ids = np.arange(self.next_id, self.next_id + len(inp.prompt_lens), dtype=np.int64)
+        self.next_id += len(ids)
+        k_dev, v_dev = inp.dev[3:] if inp.dev else (self.to_dev(inp.prompt_k),
+                                                     self.to_dev(inp.prompt_v))
+        return {"finished": self.lanes[inp.finishing], "admit_ids": ids,
+                "admit_lens": inp.prompt_lens, "prompt_key": k_dev, "prompt_value": v_dev}
+
     def run_step(self, k_step: int):
         return self.step(k_step)
 
@@ -331,7 +396,7 @@ class SharedPrefix(StepMix):
     whole group."""
 
     def __init__(self, seed: int, steps: int | None = None, device="cuda",
-                 keep_records=False, shared_decode=False):
+                 keep_records=False, shared_decode=False, native=False):
         self.shared_decode = bool(shared_decode)
         self.ws_shared = None
         spec = workloads.SHARED_PREFIX
@@ -339,7 +404,8 @@ class SharedPrefix(StepMix):
         steps = steps or spec.steps
         lens = draws.prompt_lens()
         mb = -(-(int(lens.max()) + steps) // spec.block_size)
-        super().__init__(spec, draws, steps, mb, device, keep_records)
+        super().__init__(spec, draws, steps, mb, device, keep_records, native=native,
+                         max_groups=spec.num_seqs)
         k, v = draws.prompt_kv(-1, lens)
         slots = np.empty(int(lens.sum()) + 1, dtype=np.int32)
         leaders = self._admit(lens, slots)
@@ -366,6 +432,11 @@ class SharedPrefix(StepMix):
             prefix[r0:r0 + n] = (self.manager.shared_prefix_blocks(self.lanes[r0:r0 + n]) *
                                  self.spec.block_size)
         return starts, prefix
+
+    def _native_groups(self):
+        if not self.shared_decode:
+            return None
+        return np.arange(0, len(self.lanes) + 1, self.draws.samples, dtype=np.int32)
 
     def _decode_call(self, k_step, st, tables, ctx, o_tables, o_ctx, max_ctx):
         if not self.shared_decode:

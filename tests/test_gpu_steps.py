@@ -1,4 +1,6 @@
-"""Step mixes on the GPU, replayed step by step through the CPU oracle.
+"""Step mixes on the GPU, replayed step by step through the CPU oracle; each mix is
+driven once from Python (one binding call per operation) and once by the native
+decode-step executor (one call per step).
 
 The oracle keeps its own host pools and applies every block copy and append the
 step fed to the device; slots are recomputed from the block tables alone; decode
@@ -63,9 +65,13 @@ def replay(mix, decode_steps, pool_steps):
     return worst
 
 
-def test_continuous_batching_all_steps():
+DRIVERS = [pytest.param(False, id="python-driver"), pytest.param(True, id="native-executor")]
+
+
+@pytest.mark.parametrize("native", DRIVERS)
+def test_continuous_batching_all_steps(native):
     from paged_kv_cache_414_amd import steps
-    mix = steps.ContinuousBatching(seed=3, keep_records=True)
+    mix = steps.ContinuousBatching(seed=3, keep_records=True, native=native)
     mix.prepare()  # the staged path: inputs placed in HBM before the first step
     worst = replay(mix, decode_steps=set(range(mix.steps)), pool_steps={0, 1, 25, mix.steps - 1})
     print(f"continuous batching: worst max-abs err {worst:.3e}")
@@ -76,9 +82,10 @@ def test_continuous_batching_all_steps():
     assert mix.copies_total == 0
 
 
-def test_shared_prefix_copy_on_write():
+@pytest.mark.parametrize("native", DRIVERS)
+def test_shared_prefix_copy_on_write(native):
     from paged_kv_cache_414_amd import steps
-    mix = steps.SharedPrefix(seed=4, keep_records=True)
+    mix = steps.SharedPrefix(seed=4, keep_records=True, native=native)
     last = mix.steps - 1
     worst = replay(mix, decode_steps={0, 1, 2, 15, 100, last}, pool_steps={0, 1, last})
     print(f"shared prefix: worst max-abs err {worst:.3e}")
@@ -91,11 +98,12 @@ def test_shared_prefix_copy_on_write():
     assert np.all(rc[shared_full] == 8)
 
 
-def test_shared_prefix_mix_with_shared_decode():
+@pytest.mark.parametrize("native", DRIVERS)
+def test_shared_prefix_mix_with_shared_decode(native):
     """The same mix with the decode run by pa_decode_shared_prefix: the 64 full prompt
     blocks of each group are read once for its 8 samples."""
     from paged_kv_cache_414_amd import steps
-    mix = steps.SharedPrefix(seed=4, keep_records=True, shared_decode=True)
+    mix = steps.SharedPrefix(seed=4, keep_records=True, shared_decode=True, native=native)
     last = mix.steps - 1
     worst = replay(mix, decode_steps={0, 1, 2, 15, 100, last}, pool_steps={last})
     print(f"shared prefix, shared decode: worst max-abs err {worst:.3e}")

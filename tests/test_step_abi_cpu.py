@@ -1,0 +1,74 @@
+"""The decode-step executor's C ABI on the CPU: the ctypes mirrors of the structs of
+include/pa_step.h match the C layout (a small C program prints sizes and offsets),
+and creation and step calls reject bad arguments before touching a GPU."""
+
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+
+
+@pytest.fixture(scope="module")
+def c_layout(tmp_path_factory):
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    exe = tmp_path_factory.mktemp("layout") / "step_layout"
+    subprocess.run([cc, "-std=c99", "-Wall", f"-I{ROOT / 'include'}", "-o", str(exe),
+                    str(ROOT / "tests" / "native" / "step_layout.c")], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    return {k: int(v) for k, v in (line.split() for line in out.splitlines())}
+
+
+def test_struct_layouts_match_the_header(c_layout):
+    from paged_kv_cache_414_amd import engine
+    mirrors = {"pa_step_config": engine._Config, "pa_step_args": engine._Args,
+               "pa_step_result": engine.StepResult, "pa_step_view": engine._View}
+    for c_name, py in mirrors.items():
+        assert ctypes.sizeof(py) == c_layout[c_name], c_name
+        for field, _ in py._fields_:
+            assert getattr(py, field).offset == c_layout[f"{c_name}.{field}"], (c_name, field)
+        assert {f for f, _ in py._fields_} == {k.split(".")[1] for k in c_layout
+                                                if k.startswith(c_name + ".")}
+
+
+def _config(engine, **kw):
+    base = dict(num_heads=4, head_dim=64, dtype=1, max_seqs=8, max_blocks_per_seq=16,
+                max_admit_tokens=0, max_groups=0)
+    base.update(kw)
+    return engine._Config(**base)
+
+
+def test_create_rejects_bad_configurations():
+    from paged_kv_cache_414_amd import blocks, engine, ops
+    lib = ops.lib
+    fake = 1 << 40  # never dereferenced: every call below fails validation first
+    bm = blocks.BlockManager(64, 16)
+    assert not lib.pa_step_create(None, ctypes.byref(_config(engine)), fake, fake)
+    assert b"NULL" in lib.pa_last_error()
+    for kw, text in (({"head_dim": 72}, b"head_dim"), ({"dtype": 5}, b"dtype"),
+                     ({"max_seqs": 0}, b"max_seqs"), ({"max_groups": -1}, b"max_groups"),
+                     ({"max_admit_tokens": -3}, b"max_admit_tokens")):
+        assert not lib.pa_step_create(bm._h, ctypes.byref(_config(engine, **kw)), fake, fake)
+        assert text in lib.pa_last_error(), kw
+    odd = blocks.BlockManager(64, 24)  # a block size pa_decode is not built for
+    assert not lib.pa_step_create(odd._h, ctypes.byref(_config(engine)), fake, fake)
+    assert b"block_size" in lib.pa_last_error()
+    huge = blocks.BlockManager(64, 256)
+    cfg = _config(engine, max_blocks_per_seq=1 << 24)
+    assert not lib.pa_step_create(huge._h, ctypes.byref(cfg), fake, fake)
+    assert b"int32" in lib.pa_last_error()
+
+
+def test_run_and_last_reject_null_handles():
+    from paged_kv_cache_414_amd import engine, ops
+    args = engine._Args()
+    assert ops.lib.pa_step_run(None, ctypes.byref(args), None, None) == 1
+    assert ops.lib.pa_step_last(None, ctypes.byref(engine._View())) == 1
+    ops.lib.pa_step_destroy(None)  # a no-op

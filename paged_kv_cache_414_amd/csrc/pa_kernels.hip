@@ -841,19 +841,6 @@ __global__ __launch_bounds__(256) void block_copy_kernel(CopyParams prm) {
 }
 
 // ---------------------------------------------------------------------------------
-// staging copy: pinned host memory -> device memory, one 16-byte word per thread
-// ---------------------------------------------------------------------------------
-// The decode-step executor moves each step's small arrays with this kernel rather
-// than with an asynchronous copy by the DMA engines: the kernels that read the arrays
-// then follow it in the same queue, with no hand-over between engines per step.
-
-__global__ __launch_bounds__(256) void stage_copy_kernel(const u32x4* src, u32x4* dst, int64_t words) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    dst[i] = src[i];
-}
-
-// ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
 
@@ -968,16 +955,6 @@ hipError_t launch_block_copy(const CopyParams& prm, hipStream_t stream) {
   if (gy > 1024) gy = 1024;
   hipLaunchKernelGGL(block_copy_kernel, dim3(prm.num_pairs, static_cast<unsigned>(gy)), dim3(256), 0,
                      stream, prm);
-  return hipGetLastError();
-}
-
-hipError_t launch_stage_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
-  const int64_t words = bytes / 16;
-  if (words <= 0) return hipSuccess;
-  int64_t groups = (words + 255) / 256;
-  if (groups > 64) groups = 64;
-  hipLaunchKernelGGL(stage_copy_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0, stream,
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), words);
   return hipGetLastError();
 }
 

@@ -99,6 +99,11 @@ hipError_t launch_block_copy(const CopyParams& prm, hipStream_t stream);
 // bytes / 16 words from `src` (device-visible pinned host memory) to `dst` (device);
 // bytes a multiple of 16, both 16-byte aligned.
 hipError_t launch_stage_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+// The staging copy and the slot-mapped append of `append` in one launch: the
+// append's slot_mapping is read from the pinned host buffer itself (device view),
+// not from the staged copy being written by the same launch.
+hipError_t launch_stage_copy_append(const void* src, void* dst, int64_t bytes, const AppendParams& append,
+                                    hipStream_t stream);
 
 }  // namespace pa
 

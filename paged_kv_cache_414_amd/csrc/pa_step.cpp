@@ -20,6 +20,8 @@ constexpr int64_t kAlign = 4;  // int32 elements: every staged array starts 16-b
 
 int64_t aligned(int64_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 pa_status hip_fail(hipError_t err, const char* what) {
   return pa::set_error(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
@@ -92,6 +94,10 @@ pa_step_engine* pa_step_create(pa_block_manager* bm, const pa_step_config* confi
                                void* value_cache) {
   if (!bm || !config || !key_cache || !value_cache) {
     pa::set_error(PA_ERR_NULL, "manager, config and both pools must not be NULL");
+    return nullptr;
+  }
+  if (!aligned16(key_cache) || !aligned16(value_cache)) {
+    pa::set_error(PA_ERR_INVALID_ARG, "pools must be 16-byte aligned");
     return nullptr;
   }
   const pa_step_config& c = *config;
@@ -169,6 +175,9 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
     return pa::set_error(PA_ERR_INVALID_ARG, "num_seqs %d outside [1, %d]", n, c.max_seqs);
   if (!a->seq_ids || !a->query || !a->new_key || !a->new_value || !a->out)
     return pa::set_error(PA_ERR_NULL, "seq_ids, query, new_key, new_value and out must not be NULL");
+  if (!aligned16(a->query) || !aligned16(a->new_key) || !aligned16(a->new_value) || !aligned16(a->out) ||
+      !aligned16(a->prompt_key) || !aligned16(a->prompt_value))
+    return pa::set_error(PA_ERR_INVALID_ARG, "query, rows, out and prompt rows must be 16-byte aligned");
   if (a->num_groups < 0 || a->num_groups > c.max_groups)
     return pa::set_error(PA_ERR_INVALID_ARG, "num_groups %d outside [0, %d]", a->num_groups, c.max_groups);
   const int32_t g_count = a->num_groups;
@@ -280,17 +289,32 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
     if (admitted > 0) pa_bm_add_sequences(e->bm, a->admit_ids, a->admit_lens, admitted, h + e->off_admit);
   }
 
-  // ---- 4. one copy of the staged arrays, by a kernel on the step's stream ----
+  // ---- 4. one copy of the staged arrays, by a kernel on the step's stream; with no
+  // copy-on-write due, the append of the step's rows runs in the same launch ----
+  const int32_t H = c.num_heads, D = c.head_dim, NB = e->num_blocks;
   const int64_t used = aligned(admitted_tokens > 0 ? e->off_admit + admitted_tokens : e->off_admit);
-  err = pa::launch_stage_copy(e->host_dev[t], e->dev, used * static_cast<int64_t>(sizeof(int32_t)),
-                              static_cast<hipStream_t>(stream));
+  const int64_t used_bytes = used * static_cast<int64_t>(sizeof(int32_t));
+  if (copies == 0) {
+    pa::AppendParams ap;
+    ap.key_cache = e->key_cache;
+    ap.value_cache = e->value_cache;
+    ap.key = a->new_key;
+    ap.value = a->new_value;
+    ap.slot_mapping = static_cast<const int32_t*>(e->host_dev[t]) + e->off_slots;
+    ap.num_tokens = n;
+    ap.num_heads = H;
+    ap.block_size = bs;
+    ap.row_bytes = D * (c.dtype == PA_F16 ? 2 : 4);
+    err = pa::launch_stage_copy_append(e->host_dev[t], e->dev, used_bytes, ap, static_cast<hipStream_t>(stream));
+  } else {
+    err = pa::launch_stage_copy(e->host_dev[t], e->dev, used_bytes, static_cast<hipStream_t>(stream));
+  }
   if (err == hipSuccess) err = hipEventRecord(e->copied[t], static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "pa_step_run: staging copy");
   e->in_flight[t] = true;
   e->turn ^= 1;
 
   // ---- 5. kernels, in stream order ----
-  const int32_t H = c.num_heads, D = c.head_dim, NB = e->num_blocks;
   const size_t need_ws =
       g_count > 0 ? pa_decode_shared_prefix_workspace_bytes(n, H, D, bs, g_count, max_prefix, max_suffix, 0, 0)
                   : pa_decode_workspace_bytes(n, H, D, bs, max_ctx, 0);
@@ -306,14 +330,14 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
     if (err != hipSuccess) return hip_fail(err, "pa_step_run: decode workspace");
     e->workspace_bytes = grown;
   }
-  if (copies > 0) {
+  if (copies > 0) {  // the copies first: the new rows go into the fresh private blocks
     st = pa_block_copy(e->key_cache, e->value_cache, e->dev_at(e->off_pairs), copies, H, D, bs, NB, c.dtype,
                        stream);
     if (st != PA_OK) return st;
+    st = pa_cache_append(e->key_cache, e->value_cache, a->new_key, a->new_value, e->dev_at(e->off_slots), n, H,
+                         D, bs, NB, c.dtype, stream);
+    if (st != PA_OK) return st;
   }
-  st = pa_cache_append(e->key_cache, e->value_cache, a->new_key, a->new_value, e->dev_at(e->off_slots), n, H, D,
-                       bs, NB, c.dtype, stream);
-  if (st != PA_OK) return st;
   if (g_count > 0) {
     st = pa_decode_shared_prefix(a->out, a->query, e->key_cache, e->value_cache, e->dev_at(e->off_tables),
                                  e->dev_at(e->off_ctx), e->dev_at(e->off_starts), e->dev_at(e->off_prefix), n, H,

@@ -14,7 +14,9 @@ small array the device needs is written straight into one pinned staging buffer
 (two, used in turn) and moved with one asynchronous copy.  Device side, all on the
 current stream: pa_block_copy (only when copy-on-write pairs are due),
 pa_cache_append of the step's rows, the decode (pa_decode, or
-pa_decode_shared_prefix), then pa_cache_append of admitted prompts.  After
+pa_decode_shared_prefix), then pa_cache_append of admitted prompts.  With
+``native=True`` the whole step is one call of the decode-step executor
+(include/pa_step.h, :mod:`engine`), which does the same in the same order.  After
 :meth:`StepMix.prepare`, every step's synthetic inputs (new K/V rows, queries,
 prompts) already sit in HBM.
 

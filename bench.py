@@ -291,14 +291,17 @@ def shared_prefix_decode(torch, ops, metrics, args):
     starts, prefix = dev(b.group_starts), dev(b.prefix_lens)
     out = torch.empty_like(q)
     ws = ops.workspace_for(q, k, b.max_context_len, 0)
-    ws2 = ops.shared_prefix_workspace_for(q, k, b.num_groups, b.max_prefix_len, b.max_suffix_len)
+    largest = int(np.diff(b.group_starts).max())
+    ws2 = ops.shared_prefix_workspace_for(q, k, b.num_groups, b.max_prefix_len, b.max_suffix_len,
+                                          max_group_size=largest)
 
     def plain():
         ops.pa_decode(out, q, k, v, tables, ctx, b.scale, b.max_context_len, 0, ws)
 
     def shared():
         ops.pa_decode_shared_prefix(out, q, k, v, tables, ctx, starts, prefix, b.scale,
-                                    b.max_prefix_len, b.max_suffix_len, workspace=ws2)
+                                    b.max_prefix_len, b.max_suffix_len, workspace=ws2,
+                                    max_group_size=largest)
 
     for _ in range(10):
         plain()

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum pa_dtype {
   PA_F32 = 0,
@@ -266,10 +266,16 @@ pa_status pa_swap_blocks(void* dst_key, void* dst_value, const void* src_key,
  *                  For every sequence of group g, the first prefix_lens[s] /
  *                  block_size entries of its block table equal those of sequence
  *                  group_starts[g].
+ *   max_group_size host: the number of members of the largest group, or 0 for
+ *                  the library's choice (the average group size).  Any value >= 0
+ *                  gives the same result; it sizes the launch: each tile of 16
+ *                  members of a group gets its own workgroups, and a group larger
+ *                  than max_group_size walks its further tiles in turn.
  *   max_prefix_len host: >= every prefix_lens[s], a multiple of block_size.
  *   max_suffix_len host: >= every context_lens[s] - prefix_lens[s].
  * Both are <= max_blocks_per_seq * block_size, and every context_lens[s] is too.
- * Groups of any size are accepted; a group's prefix is read once per 16 members.
+ * Groups of any size are accepted; a group's prefix is read once per 16 members, by
+ * workgroups that run side by side.
  * Built for PA_F16, head_dim in {64, 128} and block_size in {16, 32, 64, 128, 256};
  * other values return PA_ERR_UNSUPPORTED.  partition_size applies to the tokens after the prefix
  * (as in pa_decode, sized by max_suffix_len); prefix_partition_size is the number
@@ -292,8 +298,8 @@ pa_status pa_swap_blocks(void* dst_key, void* dst_value, const void* src_key,
  */
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                                int32_t head_dim, int32_t block_size,
-                                               int32_t num_groups, int32_t max_prefix_len,
-                                               int32_t max_suffix_len,
+                                               int32_t num_groups, int32_t max_group_size,
+                                               int32_t max_prefix_len, int32_t max_suffix_len,
                                                int32_t partition_size,
                                                int32_t prefix_partition_size);
 
@@ -303,10 +309,11 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_
                                   const int32_t* prefix_lens, int32_t num_seqs,
                                   int32_t num_heads, int32_t head_dim, int32_t block_size,
                                   int32_t num_blocks, int32_t max_blocks_per_seq,
-                                  int32_t num_groups, int32_t max_prefix_len,
-                                  int32_t max_suffix_len, float scale, pa_dtype dtype,
-                                  int32_t partition_size, int32_t prefix_partition_size,
-                                  void* workspace, size_t workspace_bytes, void* stream);
+                                  int32_t num_groups, int32_t max_group_size,
+                                  int32_t max_prefix_len, int32_t max_suffix_len, float scale,
+                                  pa_dtype dtype, int32_t partition_size,
+                                  int32_t prefix_partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

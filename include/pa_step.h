@@ -115,6 +115,7 @@ typedef struct pa_step_result {
   int32_t max_context_len;  /* longest context of the step, the new token counted */
   int32_t max_prefix_len;   /* groups given: longest shared prefix (tokens); else 0 */
   int32_t max_suffix_len;   /* groups given: longest context after the prefix; else 0 */
+  int32_t max_group_size;   /* groups given: members of the largest group; else 0 */
 } pa_step_result;
 
 /* One decode step (steps 1-5 above); `result` (may be NULL) receives its counts.

@@ -204,17 +204,32 @@ pa_status plan_decode(DecodePlan* plan, void* out, const void* query, const void
 }
 
 // Library choice of the prefix partition length (tokens of the shared prefix that
-// one workgroup reads for all of a group's queries): the whole longest prefix,
-// halved while fewer than kPrefixMinUnits (group, head, partition) workgroups -- one
-// per compute unit -- would be launched, as long as the half stays at or above
-// kPrefixMinTokens.  Measured on MI355X (8 groups x 32 heads, 1024 shared tokens):
-// one partition per (group, head) beats 2, 4 and 8 (76.6, 79.3, 81, 93 us).
+// one workgroup reads for a tile of 16 of a group's queries): the whole longest
+// prefix, halved while fewer than kPrefixMinUnits (group, query tile, head,
+// partition) workgroups -- one per compute unit -- would be launched, as long as the
+// half stays at or above kPrefixMinTokens.  Measured on MI355X (8 groups x 32 heads,
+// 1024 shared tokens): one partition per (group, head) beats 2, 4 and 8 (76.6,
+// 79.3, 81, 93 us).
 constexpr int64_t kPrefixMinUnits = 256;
 constexpr int32_t kPrefixMinTokens = 64;
-constexpr int32_t kPrefixTile = 16;  // tokens per matrix-core tile of the prefix pass
+constexpr int32_t kPrefixTile = 16;  // tokens per matrix-core tile of the prefix pass,
+                                     // and queries per query tile
 
-int32_t resolve_prefix_partition(int32_t num_groups, int32_t num_heads, int32_t block_size,
-                                 int32_t max_prefix_len, int32_t prefix_partition_size) {
+// Query tiles (16 members each) launched per group: enough for the largest group,
+// as given, or for the average group when max_group_size is 0; within the grid's
+// z limit.  Groups with more tiles than this loop over the rest in the workgroup.
+int32_t prefix_query_tiles(int32_t num_seqs, int32_t num_groups, int32_t max_group_size) {
+  if (num_groups <= 0) return 1;
+  const int64_t members = max_group_size > 0 ? max_group_size : (static_cast<int64_t>(num_seqs) + num_groups - 1) / num_groups;
+  int64_t tiles = (members + kPrefixTile - 1) / kPrefixTile;
+  if (tiles < 1) tiles = 1;
+  const int64_t cap = kMaxGridYZ / num_groups;
+  return static_cast<int32_t>(tiles < cap ? tiles : (cap > 0 ? cap : 1));
+}
+
+int32_t resolve_prefix_partition(int32_t num_groups, int32_t query_tiles, int32_t num_heads,
+                                 int32_t block_size, int32_t max_prefix_len,
+                                 int32_t prefix_partition_size) {
   const int32_t unit = block_size > kPrefixTile ? block_size : kPrefixTile;
   if (prefix_partition_size < 0 || (prefix_partition_size > 0 && prefix_partition_size % unit != 0)) {
     fail(PA_ERR_INVALID_ARG, "prefix_partition_size %d must be 0 or a positive multiple of %d",
@@ -222,7 +237,8 @@ int32_t resolve_prefix_partition(int32_t num_groups, int32_t num_heads, int32_t 
     return -1;
   }
   if (prefix_partition_size > 0) return prefix_partition_size;
-  const int64_t pairs = static_cast<int64_t>(num_groups > 0 ? num_groups : 1) * (num_heads > 0 ? num_heads : 1);
+  const int64_t pairs = static_cast<int64_t>(num_groups > 0 ? num_groups : 1) * query_tiles *
+                       (num_heads > 0 ? num_heads : 1);
   const int32_t floor_p = round_up(kPrefixMinTokens, unit);
   int32_t P = round_up(max_prefix_len > 0 ? max_prefix_len : 1, unit);
   while (P > floor_p) {
@@ -237,14 +253,15 @@ int32_t resolve_prefix_partition(int32_t num_groups, int32_t num_heads, int32_t 
 
 struct SharedPlan {
   int32_t Pp, NPp;  // prefix pass
+  int32_t QT;       // query tiles per group in the prefix pass's grid
   int32_t P, NPs;   // pass over the tokens after the prefix
   int32_t slots;    // NPp + NPs states per (sequence, head)
   size_t ws_bytes;
 };
 
 pa_status plan_shared(SharedPlan* plan, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                      int32_t block_size, int32_t num_groups, int32_t max_prefix_len,
-                      int32_t max_suffix_len, int32_t partition_size,
+                      int32_t block_size, int32_t num_groups, int32_t max_group_size,
+                      int32_t max_prefix_len, int32_t max_suffix_len, int32_t partition_size,
                       int32_t prefix_partition_size) {
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 128)", head_dim);
@@ -260,12 +277,15 @@ pa_status plan_shared(SharedPlan* plan, int32_t num_seqs, int32_t num_heads, int
     return fail(PA_ERR_INVALID_ARG, "max_prefix_len %d must be a non-negative multiple of block_size %d",
                 max_prefix_len, block_size);
   if (max_suffix_len < 0) return fail(PA_ERR_INVALID_ARG, "max_suffix_len %d is negative", max_suffix_len);
-  const int32_t Pp = resolve_prefix_partition(num_groups, num_heads, block_size, max_prefix_len,
+  if (max_group_size < 0) return fail(PA_ERR_INVALID_ARG, "max_group_size %d is negative", max_group_size);
+  const int32_t QT = prefix_query_tiles(num_seqs, num_groups, max_group_size);
+  const int32_t Pp = resolve_prefix_partition(num_groups, QT, num_heads, block_size, max_prefix_len,
                                               prefix_partition_size);
   if (Pp < 0) return PA_ERR_INVALID_ARG;
   const int32_t P = resolve_partition(num_seqs, num_heads, block_size, max_suffix_len, partition_size);
   if (P < 0) return PA_ERR_INVALID_ARG;
   plan->Pp = Pp;
+  plan->QT = QT;
   plan->NPp = max_prefix_len > 0 ? partitions_for(max_prefix_len, Pp) : 0;
   plan->P = P;
   plan->NPs = partitions_for(max_suffix_len, P);
@@ -483,11 +503,12 @@ pa_status pa_swap_blocks(void* dst_key, void* dst_value, const void* src_key, co
 
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                                int32_t block_size, int32_t num_groups,
-                                               int32_t max_prefix_len, int32_t max_suffix_len,
-                                               int32_t partition_size, int32_t prefix_partition_size) {
+                                               int32_t max_group_size, int32_t max_prefix_len,
+                                               int32_t max_suffix_len, int32_t partition_size,
+                                               int32_t prefix_partition_size) {
   SharedPlan plan;
-  if (plan_shared(&plan, num_seqs, num_heads, head_dim, block_size, num_groups, max_prefix_len,
-                  max_suffix_len, partition_size, prefix_partition_size) != PA_OK)
+  if (plan_shared(&plan, num_seqs, num_heads, head_dim, block_size, num_groups, max_group_size,
+                  max_prefix_len, max_suffix_len, partition_size, prefix_partition_size) != PA_OK)
     return 0;
   return plan.ws_bytes;
 }
@@ -498,15 +519,15 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_
                                   const int32_t* prefix_lens, int32_t num_seqs, int32_t num_heads,
                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                   int32_t max_blocks_per_seq, int32_t num_groups,
-                                  int32_t max_prefix_len, int32_t max_suffix_len, float scale,
-                                  pa_dtype dtype, int32_t partition_size,
-                                  int32_t prefix_partition_size, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  int32_t max_group_size, int32_t max_prefix_len,
+                                  int32_t max_suffix_len, float scale, pa_dtype dtype,
+                                  int32_t partition_size, int32_t prefix_partition_size,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != PA_F16)
     return fail(PA_ERR_UNSUPPORTED, "the shared-prefix decode is built for PA_F16 only (dtype %d)", (int)dtype);
   SharedPlan plan;
-  pa_status st = plan_shared(&plan, num_seqs, num_heads, head_dim, block_size, num_groups, max_prefix_len,
-                             max_suffix_len, partition_size, prefix_partition_size);
+  pa_status st = plan_shared(&plan, num_seqs, num_heads, head_dim, block_size, num_groups, max_group_size,
+                             max_prefix_len, max_suffix_len, partition_size, prefix_partition_size);
   if (st != PA_OK) return st;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0)
     return fail(PA_ERR_INVALID_ARG, "num_blocks %d and max_blocks_per_seq %d must be positive", num_blocks,
@@ -551,6 +572,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_
     pp.partition_tokens = plan.Pp;
     pp.num_partitions = plan.NPp;
     pp.num_groups = num_groups;
+    pp.query_tiles = plan.QT;
     pp.slots_per_pair = plan.slots;
     pp.scale = scale;
     st = from_hip(pa::launch_decode_prefix(pp, head_dim, block_size, hs), "shared-prefix pass launch");

@@ -526,7 +526,8 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(ReduceParams prm) {
 
 // ---------------------------------------------------------------------------------
 // decode, prefix pass of the shared-prefix decode (fp16): grid (prefix partitions,
-// heads, groups), kPrefixThreads threads.
+// heads, groups x query tiles), kPrefixThreads threads; a query tile is 16 members
+// of a group.
 //
 // A group is a range of sequences whose first prefix_len tokens live in the same
 // physical blocks (shared by reference count).  Each shared block is read once for
@@ -592,7 +593,8 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
 
   const int part = blockIdx.x;
   const int head = blockIdx.y;
-  const int grp = blockIdx.z;
+  const int grp = blockIdx.z / prm.query_tiles;
+  const int qtile = blockIdx.z % prm.query_tiles;  // first tile of 16 queries of this workgroup
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int c16 = lane % kTile;  // K row and query column of this lane
@@ -600,7 +602,7 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
 
   const int s0 = prm.group_starts[grp];
   const int n_seqs = prm.group_starts[grp + 1] - s0;
-  if (n_seqs <= 0) return;
+  if (qtile * kTile >= n_seqs) return;  // an empty group, or a tile past its members
   const int plen = prm.prefix_lens[s0];
   const int P = prm.partition_tokens;
   const int tok_begin = part * P;
@@ -620,7 +622,9 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
   __shared__ float s_l[kPrefixSlots][kTile];
   __shared__ float s_o[kPrefixSlots][kTile][D + 1];  // +1: rows of one lane group hit distinct banks
 
-  for (int q0 = 0; q0 < n_seqs; q0 += kTile) {
+  // Tiles qtile, qtile + query_tiles, ...: with query_tiles at least the group size
+  // / 16 (the usual case) one tile, every tile of the group in a workgroup of its own.
+  for (int q0 = qtile * kTile; q0 < n_seqs; q0 += prm.query_tiles * kTile) {
     // B operand of the score product: query q0 + c16, dims [32c + 8j, +8) per step c
     u32x4 qv[kQLoads];
     if (q0 + c16 < n_seqs) {
@@ -909,7 +913,7 @@ hipError_t launch_decode_reduce(const ReduceParams& prm, bool f16, int head_dim,
 
 template <int D>
 static hipError_t launch_prefix_d(const PrefixParams& prm, int block_size, hipStream_t stream) {
-  dim3 grid(prm.num_partitions, prm.num_heads, prm.num_groups);
+  dim3 grid(prm.num_partitions, prm.num_heads, prm.num_groups * prm.query_tiles);
   switch (block_size) {
     case 16:
       hipLaunchKernelGGL((decode_prefix_kernel<D, 16>), grid, dim3(kPrefixThreads), 0, stream, prm);

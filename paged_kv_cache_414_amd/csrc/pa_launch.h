@@ -31,7 +31,8 @@ struct DecodeParams {
 };
 
 // Prefix pass of the shared-prefix decode: one workgroup per (prefix partition,
-// head, group); groups are ranges of sequences that share leading blocks.
+// head, group, tile of 16 of the group's queries); groups are ranges of sequences
+// that share leading blocks.
 struct PrefixParams {
   const void* query;
   const void* key_cache;
@@ -46,7 +47,8 @@ struct PrefixParams {
   int32_t max_blocks_per_seq;
   int32_t partition_tokens;  // a multiple of 16 and of the block size
   int32_t num_partitions;    // grid.x
-  int32_t num_groups;        // grid.z
+  int32_t num_groups;        // grid.z = num_groups * query_tiles
+  int32_t query_tiles;       // workgroups per (partition, head, group): 16 members each
   int32_t slots_per_pair;
   float scale;
 };

@@ -256,13 +256,14 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
     ctx[i] = e->positions[i] + 1;
     max_ctx = std::max(max_ctx, ctx[i]);
   }
-  int32_t max_prefix = 0, max_suffix = 0;
+  int32_t max_prefix = 0, max_suffix = 0, max_group = 0;
   if (g_count > 0) {
     int32_t* starts = h + e->off_starts;
     int32_t* prefix = h + e->off_prefix;
     for (int32_t g = 0; g <= g_count; ++g) starts[g] = a->group_starts[g];
     for (int32_t g = 0; g < g_count; ++g) {
       const int32_t r0 = starts[g], r1 = starts[g + 1];
+      max_group = std::max(max_group, r1 - r0);
       if (r1 == r0) continue;
       const int32_t shared = pa_bm_shared_prefix_blocks(e->bm, a->seq_ids + r0, r1 - r0);
       for (int32_t r = r0; r < r1; ++r) {
@@ -316,7 +317,8 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
 
   // ---- 5. kernels, in stream order ----
   const size_t need_ws =
-      g_count > 0 ? pa_decode_shared_prefix_workspace_bytes(n, H, D, bs, g_count, max_prefix, max_suffix, 0, 0)
+      g_count > 0 ? pa_decode_shared_prefix_workspace_bytes(n, H, D, bs, g_count, max_group, max_prefix, max_suffix,
+                                                            0, 0)
                   : pa_decode_workspace_bytes(n, H, D, bs, max_ctx, 0);
   if (need_ws > e->workspace_bytes) {
     // only earlier steps used the old workspace: wait for the last of them
@@ -341,8 +343,8 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
   if (g_count > 0) {
     st = pa_decode_shared_prefix(a->out, a->query, e->key_cache, e->value_cache, e->dev_at(e->off_tables),
                                  e->dev_at(e->off_ctx), e->dev_at(e->off_starts), e->dev_at(e->off_prefix), n, H,
-                                 D, bs, NB, mb, g_count, max_prefix, max_suffix, a->scale, c.dtype, 0, 0,
-                                 e->workspace, e->workspace_bytes, stream);
+                                 D, bs, NB, mb, g_count, max_group, max_prefix, max_suffix, a->scale, c.dtype,
+                                 0, 0, e->workspace, e->workspace_bytes, stream);
   } else {
     st = pa_decode(a->out, a->query, e->key_cache, e->value_cache, e->dev_at(e->off_tables), e->dev_at(e->off_ctx),
                    n, H, D, bs, NB, mb, max_ctx, a->scale, c.dtype, 0, e->workspace, e->workspace_bytes, stream);
@@ -364,6 +366,7 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
   r.max_context_len = max_ctx;
   r.max_prefix_len = max_prefix;
   r.max_suffix_len = max_suffix;
+  r.max_group_size = max_group;
   e->last = r;
   e->has_last = true;
   e->last_turn = t;

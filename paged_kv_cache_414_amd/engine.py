@@ -41,7 +41,8 @@ class _Args(ctypes.Structure):
 
 class StepResult(ctypes.Structure):
     _fields_ = [("num_copies", _i32), ("num_admitted", _i32), ("admitted_tokens", _i32),
-                ("max_context_len", _i32), ("max_prefix_len", _i32), ("max_suffix_len", _i32)]
+                ("max_context_len", _i32), ("max_prefix_len", _i32), ("max_suffix_len", _i32),
+                ("max_group_size", _i32)]
 
 
 class _View(ctypes.Structure):
@@ -189,7 +190,7 @@ class StepEngine:
             "admit_slots": _host_array(v.admit_slots, (r.admitted_tokens,)),
             "num_copies": r.num_copies, "num_admitted": r.num_admitted,
             "max_context_len": r.max_context_len, "max_prefix_len": r.max_prefix_len,
-            "max_suffix_len": r.max_suffix_len,
+            "max_suffix_len": r.max_suffix_len, "max_group_size": r.max_group_size,
         }
 
     def decode_again(self, query, out, scale: float, stream=None) -> None:
@@ -208,8 +209,8 @@ class StepEngine:
             status = self._lib.pa_decode_shared_prefix(
                 o, q, kc, vc, v.dev_block_tables, v.dev_context_lens, v.dev_group_starts,
                 v.dev_prefix_lens, n, h, d, self.block_size, nb, self.max_blocks_per_seq,
-                v.num_groups, r.max_prefix_len, r.max_suffix_len, float(scale), dt, 0, 0,
-                v.workspace, v.workspace_bytes, s)
+                v.num_groups, r.max_group_size, r.max_prefix_len, r.max_suffix_len, float(scale),
+                dt, 0, 0, v.workspace, v.workspace_bytes, s)
         else:
             status = self._lib.pa_decode(o, q, kc, vc, v.dev_block_tables, v.dev_context_lens, n,
                                          h, d, self.block_size, nb, self.max_blocks_per_seq,

@@ -40,7 +40,7 @@ SIGNATURES = {
     "pa_cache_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                _vp]),
     "pa_block_copy": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
-    "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32] * 9),
+    "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32] * 10),
     "pa_swap_blocks": (_i32, [_vp] * 5 + [_i32] * 7 + [_vp]),
     # host block manager (include/pa_blocks.h)
     "pa_bm_create": (_vp, [_i32, _i32, ctypes.c_uint64]),
@@ -60,8 +60,8 @@ SIGNATURES = {
     "pa_bm_shared_prefix_blocks": (_i32, [_vp, _vp, _i32]),
     "pa_bm_num_seq_blocks": (_i32, [_vp, ctypes.c_int64]),
     "pa_bm_seq_blocks": (_i32, [_vp, ctypes.c_int64, _vp, _i32]),
-    "pa_decode_shared_prefix": (_i32, [_vp] * 8 + [_i32] * 9 + [_f32, _i32, _i32, _i32, _vp,
-                                                                _sz, _vp]),
+    "pa_decode_shared_prefix": (_i32, [_vp] * 8 + [_i32] * 10 + [_f32, _i32, _i32, _i32, _vp,
+                                                                 _sz, _vp]),
     # decode-step executor (include/pa_step.h); structs are passed by pointer
     "pa_step_create": (_vp, [_vp, _vp, _vp, _vp]),
     "pa_step_destroy": (None, [_vp]),
@@ -273,10 +273,11 @@ def pa_block_copy(key_cache, value_cache, block_pairs, stream=None):
 
 def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_heads, head_dim, block_size,
                                             num_groups, max_prefix_len, max_suffix_len,
-                                            partition_size=0, prefix_partition_size=0) -> int:
+                                            partition_size=0, prefix_partition_size=0,
+                                            max_group_size=0) -> int:
     n = int(lib.pa_decode_shared_prefix_workspace_bytes(
-        num_seqs, num_heads, head_dim, block_size, num_groups, max_prefix_len,
-        max_suffix_len, partition_size, prefix_partition_size))
+        num_seqs, num_heads, head_dim, block_size, num_groups, int(max_group_size),
+        max_prefix_len, max_suffix_len, partition_size, prefix_partition_size))
     if n == 0 and num_seqs > 0:
         raise PagedAttentionError(2, lib.pa_last_error().decode())
     return n
@@ -284,12 +285,13 @@ def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_heads, head_dim, block
 
 def shared_prefix_workspace_for(query, key_cache, num_groups, max_prefix_len,
                                 max_suffix_len, partition_size=0,
-                                prefix_partition_size=0) -> torch.Tensor | None:
+                                prefix_partition_size=0, max_group_size=0) -> torch.Tensor | None:
     """Device buffer of the size pa_decode_shared_prefix needs."""
     s, h, d = query.shape
     n = pa_decode_shared_prefix_workspace_bytes(s, h, d, key_cache.shape[2], num_groups,
                                                 max_prefix_len, max_suffix_len,
-                                                partition_size, prefix_partition_size)
+                                                partition_size, prefix_partition_size,
+                                                max_group_size)
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=query.device)
@@ -298,10 +300,12 @@ def shared_prefix_workspace_for(query, key_cache, num_groups, max_prefix_len,
 def pa_decode_shared_prefix(out, query, key_cache, value_cache, block_tables, context_lens,
                             group_starts, prefix_lens, scale, max_prefix_len, max_suffix_len,
                             partition_size=0, prefix_partition_size=0, workspace=None,
-                            stream=None):
+                            stream=None, max_group_size=0):
     """pa_decode for groups of sequences that share leading blocks (see include/pa.h).
 
-    group_starts int32 [G + 1] and prefix_lens int32 [S] describe the groups."""
+    group_starts int32 [G + 1] and prefix_lens int32 [S] describe the groups;
+    max_group_size (members of the largest group, 0 = library choice) sizes the launch
+    and must match the value the workspace was sized with."""
     args = list(_decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                              scale, 0, partition_size, workspace, stream))
     dev = _same_device(out, group_starts, prefix_lens)
@@ -316,7 +320,8 @@ def pa_decode_shared_prefix(out, query, key_cache, value_cache, block_tables, co
      ws_bytes, strm) = args
     _check(lib.pa_decode_shared_prefix(p_out, p_q, p_k, p_v, p_bt, p_ctx, _ptr(group_starts),
                                        _ptr(prefix_lens), s, h, d, bs, nb, mb, num_groups,
-                                       int(max_prefix_len), int(max_suffix_len), scale_f, dt,
+                                       int(max_group_size), int(max_prefix_len),
+                                       int(max_suffix_len), scale_f, dt,
                                        part, int(prefix_partition_size), p_ws, ws_bytes,
                                        _stream(stream, dev) if stream is not None else strm))
     return out

@@ -456,9 +456,10 @@ class SharedPrefix(StepMix):
         ctx_d = st.device(o_ctx, (n,))
         starts_d = st.device(o_starts, (len(starts),))
         prefix_d = st.device(o_prefix, (n,))
+        largest = int(np.diff(starts).max())
         need = ops.pa_decode_shared_prefix_workspace_bytes(
             n, self.spec.num_heads, self.spec.head_dim, self.spec.block_size, len(starts) - 1,
-            max_prefix, max_suffix)
+            max_prefix, max_suffix, max_group_size=largest)
         if self.ws_shared is None or self.ws_shared.numel() < need:
             self.ws_shared = torch.empty(need, dtype=torch.uint8, device=self.device)
         ws = self.ws_shared
@@ -466,7 +467,7 @@ class SharedPrefix(StepMix):
         def call(q_d):
             ops.pa_decode_shared_prefix(self.out, q_d, self.k_cache, self.v_cache, tables_d,
                                         ctx_d, starts_d, prefix_d, self.scale, max_prefix,
-                                        max_suffix, workspace=ws)
+                                        max_suffix, workspace=ws, max_group_size=largest)
         return call
 
     def run_step(self, k_step: int):

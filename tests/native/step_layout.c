@@ -24,6 +24,7 @@ int main(void) {
   F(pa_step_result, num_copies); F(pa_step_result, num_admitted);
   F(pa_step_result, admitted_tokens); F(pa_step_result, max_context_len);
   F(pa_step_result, max_prefix_len); F(pa_step_result, max_suffix_len);
+  F(pa_step_result, max_group_size);
   S(pa_step_view);
   F(pa_step_view, num_seqs); F(pa_step_view, num_groups); F(pa_step_view, result);
   F(pa_step_view, slots); F(pa_step_view, positions); F(pa_step_view, copy_pairs);

@@ -47,7 +47,7 @@ def test_binding_covers_every_declared_symbol(ops):
 
 
 def test_abi_version_and_status_strings(ops):
-    assert ops.lib.pa_abi_version() == 1
+    assert ops.lib.pa_abi_version() == 2
     assert ops.lib.pa_status_string(0) == b"PA_OK"
     assert ops.lib.pa_status_string(4) == b"PA_ERR_WORKSPACE"
     assert ops.lib.pa_status_string(99) == b"PA_ERR_UNKNOWN"
@@ -123,14 +123,14 @@ def test_append_and_copy_reject_bad_arguments(ops):
 def _bad_shared(ops, **over):
     p = 1 << 20
     args = dict(out=p, q=p, k=p, v=p, bt=p, ctx=p, gs=p, pl=p, S=16, H=4, D=128, bs=16, NB=64,
-                MB=8, G=2, maxp=64, maxs=64, scale=0.125, dtype=1, P=0, Pp=0, ws=p,
+                MB=8, G=2, maxg=8, maxp=64, maxs=64, scale=0.125, dtype=1, P=0, Pp=0, ws=p,
                 wsb=1 << 30)
     args.update(over)
     return ops.lib.pa_decode_shared_prefix(
         args["out"], args["q"], args["k"], args["v"], args["bt"], args["ctx"], args["gs"],
         args["pl"], args["S"], args["H"], args["D"], args["bs"], args["NB"], args["MB"],
-        args["G"], args["maxp"], args["maxs"], args["scale"], args["dtype"], args["P"],
-        args["Pp"], args["ws"], args["wsb"], None)
+        args["G"], args["maxg"], args["maxp"], args["maxs"], args["scale"], args["dtype"],
+        args["P"], args["Pp"], args["ws"], args["wsb"], None)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -145,6 +145,7 @@ def _bad_shared(ops, **over):
     (dict(Pp=24), 2),              # prefix partitions are whole 16-token tiles
     (dict(P=24), 2),
     (dict(G=-1), 2),
+    (dict(maxg=-1), 2),
     (dict(scale=float("inf")), 2),
     (dict(pl=None), 1),
     (dict(gs=None), 1),
@@ -166,8 +167,22 @@ def test_shared_prefix_planning(ops):
     slots = 4 + ops.pa_decode_num_partitions(s, h, 16, 272, 0)
     ml = -(-(s * h * slots * 4) // 256) * 256
     assert n == 2 * ml + s * h * slots * d * 4
+
+    def prefix_slots(groups, max_group_size, maxp):
+        # S*H*4 is a multiple of 256 here, so the bytes are slots x S*H*(D+2)*4 exactly
+        n = ops.pa_decode_shared_prefix_workspace_bytes(s, h, d, 16, groups, maxp, 16, 0, 0,
+                                                        max_group_size)
+        return n // (s * h * (d + 2) * 4) - ops.pa_decode_num_partitions(s, h, 16, 16, 0)
+    # the library's prefix partition: the whole prefix while (groups x 16-member tiles
+    # x heads) fills 256 workgroups, halved otherwise (not below 64 tokens)
+    assert prefix_slots(8, 8, 1024) == 1        # 8 x 1 x 32 = 256 workgroups
+    assert prefix_slots(1, 8, 1024) == 8        # 32 per partition: 8 partitions of 128
+    assert prefix_slots(1, 64, 1024) == 2       # 4 tiles x 32 = 128: 2 partitions of 512
+    assert prefix_slots(1, 0, 1024) == 2        # 0: the average group (64 members) decides
+    assert prefix_slots(2, 0, 1024) == 2        # average 32 members: 2 x 2 x 32 = 128
+    assert prefix_slots(1, 128, 512) == 1       # 8 tiles x 32 = 256 already
     # a prefix that is not a whole number of blocks is refused
-    assert ops.lib.pa_decode_shared_prefix_workspace_bytes(s, h, d, 16, 8, 1000, 272, 0, 0) == 0
+    assert ops.lib.pa_decode_shared_prefix_workspace_bytes(s, h, d, 16, 8, 0, 1000, 272, 0, 0) == 0
     assert ops.lib.pa_last_error() != b""
     with pytest.raises(ops.PagedAttentionError):
         ops.pa_decode_shared_prefix_workspace_bytes(s, h, d, 16, 8, 1000, 272)

@@ -31,19 +31,26 @@ def _gpu():
     from paged_kv_cache_414_amd import ops  # noqa: F401  (raises if not built)
 
 
-def run_shared(b, partition=0, prefix_partition=0, return_ws=False):
+def largest_group(b) -> int:
+    return int(np.diff(b.group_starts).max()) if b.num_groups else 0
+
+
+def run_shared(b, partition=0, prefix_partition=0, return_ws=False, max_group_size=None):
     from paged_kv_cache_414_amd import ops
+    if max_group_size is None:
+        max_group_size = largest_group(b)
     q, k, v = dev(b.q), dev(b.k_pool), dev(b.v_pool)
     tables, ctx = dev(b.block_tables), dev(b.context_lens)
     starts, prefix = dev(b.group_starts), dev(b.prefix_lens)
     out = torch.full_like(q, float("nan"))
     ws = ops.shared_prefix_workspace_for(q, k, b.num_groups, b.max_prefix_len, b.max_suffix_len,
-                                         partition, prefix_partition)
+                                         partition, prefix_partition, max_group_size)
     note(f"pa_decode_shared_prefix {b.name} S={b.num_seqs} H={b.num_heads} D={b.head_dim} "
-         f"bs={b.block_size} groups={b.num_groups} P={partition} Pp={prefix_partition}")
+         f"bs={b.block_size} groups={b.num_groups} P={partition} Pp={prefix_partition} "
+         f"max_group_size={max_group_size}")
     ops.pa_decode_shared_prefix(out, q, k, v, tables, ctx, starts, prefix, b.scale,
                                 b.max_prefix_len, b.max_suffix_len, partition,
-                                prefix_partition, ws)
+                                prefix_partition, ws, max_group_size=max_group_size)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     return (got, ws) if return_ws else got
@@ -171,3 +178,34 @@ def test_more_than_64_prefix_tiles_per_wave():
                                            prefix_blocks_high=580, suffix_low=1, suffix_high=50)
     got = run_shared(b, 0, 16384)
     assert max_abs_err(got, _oracle(b)) <= TOL
+
+
+def test_large_groups_match_oracle_for_any_launch_size():
+    """Groups of 64 and 100 members (7 tiles of 16, the last partly filled) plus small
+    ones: every value of max_group_size gives the oracle's result, and with the prefix
+    partition fixed the outputs are bit-identical (each query's arithmetic does not
+    depend on which workgroup walks its tile)."""
+    b = workloads.make_shared_prefix_batch("large_groups", seed=61, group_sizes=[64, 3, 100],
+                                           num_heads=4, head_dim=128, block_size=16,
+                                           prefix_blocks_low=8, prefix_blocks_high=20,
+                                           suffix_low=0, suffix_high=60, ungrouped=2)
+    want = _oracle(b)
+    outs = {}
+    for mg in (100, 0, 16, 1, 400):
+        outs[mg] = run_shared(b, prefix_partition=64, max_group_size=mg)
+        assert max_abs_err(outs[mg], want) <= TOL, mg
+    for mg in (0, 16, 1, 400):
+        assert np.array_equal(outs[mg].view(np.uint16), outs[100].view(np.uint16)), mg
+    # the library's own prefix partition, with the exact and the default launch size
+    for mg in (100, 0):
+        assert max_abs_err(run_shared(b, max_group_size=mg), want) <= TOL, mg
+
+
+def test_whole_batch_as_one_group():
+    """All 256 sequences of the batch share one prompt (a common system prompt): one
+    group, 16 tiles of 16 queries."""
+    b = workloads.make_shared_prefix_batch("one_group", seed=67, group_sizes=[256],
+                                           num_heads=2, head_dim=64, block_size=32,
+                                           prefix_blocks_low=16, prefix_blocks_high=16,
+                                           suffix_low=1, suffix_high=40)
+    assert max_abs_err(run_shared(b), _oracle(b)) <= TOL

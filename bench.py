@@ -31,14 +31,14 @@ METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 
 # HBM bytes per launch of the partition pass on this workload (seed 2), from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
-# known-size block copy (FETCH_SIZE x 1.9963, WRITE_SIZE x 1.000); the commands and
+# known-size block copy (FETCH_SIZE x 1.9964, WRITE_SIZE x 1.000); the commands and
 # raw values are in profiles/decode_partitions_llama7b_pmc.md.  Valid only for the
 # kernel source they were taken on.
 MEASURED_TRAFFIC = {
-    "kernel_source_sha256": "d92e3f0841f5a970f0cba4550ffb959a9d843120b414703ac14ca86649603e41",
+    "kernel_source_sha256": "07cdc0e722e139c93a0302cddbe9ffc5413a2925dea7ec38300bb28ff7693315",
     "seed": 2,
     "partition_tokens": 2048,
-    "read_bytes": 1934638082,
+    "read_bytes": 1934721857,
     "write_bytes": 786432,
 }
 KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -397,6 +397,57 @@ def swap_throughput(torch, ops, args, pairs=2048):
     return res
 
 
+def shared_prefix_groups(torch, ops, metrics, args):
+    """pa_decode against pa_decode_shared_prefix for other group layouts (32 heads x
+    128, block 16, fp16; each member holds 200-330 tokens of its own after the shared
+    prefix): many small groups, one group of 64 sharing a long prompt, and one group of
+    256 (a prompt shared by the whole batch)."""
+    from paged_kv_cache_414_amd import workloads
+
+    log(args, "shared-prefix group layouts")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    rows = []
+    for sizes, prefix_blocks in (([8] * 8, 64), ([64], 128), ([256], 32)):
+        b = workloads.make_shared_prefix_batch("groups", seed=3, group_sizes=sizes, num_heads=32,
+                                               head_dim=128, block_size=16,
+                                               prefix_blocks_low=prefix_blocks,
+                                               prefix_blocks_high=prefix_blocks, suffix_low=200,
+                                               suffix_high=330, poison=False)
+        q, k, v = dev(b.q), dev(b.k_pool), dev(b.v_pool)
+        tables, ctx = dev(b.block_tables), dev(b.context_lens)
+        starts, prefix = dev(b.group_starts), dev(b.prefix_lens)
+        out = torch.empty_like(q)
+        ws = ops.workspace_for(q, k, b.max_context_len, 0)
+        ws2 = ops.shared_prefix_workspace_for(q, k, b.num_groups, b.max_prefix_len,
+                                              b.max_suffix_len, max_group_size=max(sizes))
+
+        def plain():
+            ops.pa_decode(out, q, k, v, tables, ctx, b.scale, b.max_context_len, 0, ws)
+
+        def shared():
+            ops.pa_decode_shared_prefix(out, q, k, v, tables, ctx, starts, prefix, b.scale,
+                                        b.max_prefix_len, b.max_suffix_len, workspace=ws2,
+                                        max_group_size=max(sizes))
+
+        for _ in range(10):
+            plain()
+            shared()
+        n = max(20, args.steps // 2)
+        ms_plain = time_launches(plain, n, torch)
+        ms_shared = time_launches(shared, n, torch)
+        per_token = metrics.kv_bytes_per_token(1, b.num_heads, b.head_dim, 2)
+        unique = per_token * int((b.context_lens - b.prefix_lens).sum() +
+                                 b.prefix_lens[b.group_starts[:-1]].sum())
+        rows.append({"groups": f"{len(sizes)} x {sizes[0]}", "prefix_tokens": prefix_blocks * 16,
+                     "pa_decode_ms": round(ms_plain, 5),
+                     "pa_decode_shared_prefix_ms": round(ms_shared, 5),
+                     "speedup": round(ms_plain / ms_shared, 3),
+                     "shared_unique_kv_gbps": round(metrics.gbps(unique, ms_shared * 1e-3), 1)})
+        del q, k, v, tables, ctx, starts, prefix, out, ws, ws2
+        torch.cuda.empty_cache()
+    return rows
+
+
 def copy_probe(torch, ops, metrics, pairs=1024):
     """One pa_block_copy of ``pairs`` blocks of 32 heads x 16 x 128 fp16 (128 KiB per
     block for K and for V): a plain copy of known size, run once, whose memory
@@ -527,6 +578,7 @@ def main():
         record["long_context"] = long_context_decode(torch, ops, metrics, args)
         record["tiny_fp32"] = tiny_fp32_decode(torch, ops, metrics, args)
         record["shared_prefix_decode"] = shared_prefix_decode(torch, ops, metrics, args)
+        record["shared_prefix_groups"] = shared_prefix_groups(torch, ops, metrics, args)
         if args.graph:
             record["graph_step"] = graph_step(torch, ops, metrics, args)
         record["block_swap"] = swap_throughput(torch, ops, args)

@@ -583,7 +583,7 @@ def main():
         "decode_launch_ms": decode_spread,
         "kv_bytes_per_step": kv,
         "roofline": {
-            "kernel": "decode_partitions_kernel<f16, 128, 16>",
+            "kernel": "decode_partitions_kernel<f16, 128, 16, 16 waves>",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": metrics.HBM_PEAK_GBPS,

@@ -125,6 +125,36 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_heads, int32_t block_siz
   return P;
 }
 
+// Library choice of the decode workgroup: 16 wave64s rather than 8 when every wave
+// still folds about two units of the partition (32 units or more: tokens one wave
+// folds at once, the kernel's unit of work, computed below as the kernel does) and
+// the launch holds at least 1024 workgroups.  Shorter work per workgroup evens out
+// the end of a launch of many workgroups; with few workgroups, or short partitions,
+// the wide groups leave waves idle.  Measured on MI355X (fp16, 32 heads x 128, GB/s,
+// 8 / 16 waves): 96 x U[300, 2048] 6,401 / 6,563; 64 x U[1, 562] 6,024 / 6,139;
+// 32 x U[1, 1024] 5,795 / 6,280; 64 x U[400, 700] 6,345 / 6,592; but 16 x
+// U[4096, 8192] (512 workgroups) 6,424 / 6,185, 64 x U[100, 300] (19 units) 6,022 /
+// 5,437 and 256 x U[1, 256] 6,375 / 4,875.
+constexpr int32_t kWideMinUnits = 32;
+constexpr int64_t kWideMinWorkgroups = 1024;
+
+int32_t unit_tokens(pa_dtype dtype, int32_t head_dim, int32_t block_size) {
+  const int32_t vec = dtype == PA_F16 ? 8 : 4;  // elements per 16-byte load
+  int32_t lanes = 1;                            // lanes per token row: a power of two
+  while (lanes < head_dim / vec) lanes *= 2;
+  const int32_t rows_per_load = 64 / lanes;
+  const int32_t most = rows_per_load * 8;       // at most 8 loads per unit
+  return block_size < most ? block_size : most;
+}
+
+bool wide_workgroups(pa_dtype dtype, int32_t head_dim, int32_t block_size, int32_t P, int32_t num_seqs,
+                     int32_t num_heads, int32_t NP) {
+  const int32_t unit = unit_tokens(dtype, head_dim, block_size);
+  const int64_t units = (static_cast<int64_t>(P) + unit - 1) / unit;
+  const int64_t groups = static_cast<int64_t>(num_seqs) * num_heads * NP;
+  return units >= kWideMinUnits && groups >= kWideMinWorkgroups;
+}
+
 int32_t partitions_for(int32_t max_context_len, int32_t P) {
   const int64_t np = (static_cast<int64_t>(max_context_len) + P - 1) / P;
   return np < 1 ? 1 : static_cast<int32_t>(np);
@@ -199,6 +229,7 @@ pa_status plan_decode(DecodePlan* plan, void* out, const void* query, const void
   p.slots_per_pair = NP;
   p.slot_offset = 0;
   p.prefix_partition_tokens = P;
+  p.wide = wide_workgroups(dtype, head_dim, block_size, P, num_seqs, num_heads, NP) ? 1 : 0;
   p.scale = scale;
   return PA_OK;
 }
@@ -598,6 +629,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_
   dp.slots_per_pair = plan.slots;
   dp.slot_offset = plan.NPp;
   dp.prefix_partition_tokens = plan.Pp;
+  dp.wide = wide_workgroups(PA_F16, head_dim, block_size, plan.P, num_seqs, num_heads, plan.NPs) ? 1 : 0;
   dp.scale = scale;
   st = from_hip(pa::launch_decode_partitions(dp, true, head_dim, block_size, hs), "suffix pass launch");
   if (st != PA_OK) return st;

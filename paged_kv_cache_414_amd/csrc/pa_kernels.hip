@@ -9,8 +9,8 @@
 // (block, head) form one contiguous chunk of block_size * head_dim elements
 // (4 KiB for 16 tokens x 128 dims in fp16).
 //
-// Decode (partition pass).  One workgroup of kWaves wave64s per (partition, head,
-// sequence).  A partition is P consecutive tokens of one sequence; its blocks are
+// Decode (partition pass).  One workgroup of W wave64s (8 or 16, chosen per launch)
+// per (partition, head, sequence).  A partition is P consecutive tokens of one sequence; its blocks are
 // dealt to the waves round-robin.  Within a wave every lane loads 16 bytes per
 // instruction, so one wave-wide load covers a contiguous 1 KiB of a chunk:
 // kTokPerLoad token rows of kLanesPerTok lanes each.  A lane therefore always holds
@@ -37,7 +37,10 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Build-time tuning knobs (defaults are the measured best on MI355X).
 #ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 8  // wave64s per decode workgroup
+#define PA_DECODE_WAVES 8  // wave64s per decode workgroup, short partitions or few workgroups
+#endif
+#ifndef PA_DECODE_WAVES_WIDE
+#define PA_DECODE_WAVES_WIDE 16  // wave64s per decode workgroup otherwise
 #endif
 #ifndef PA_KV_LOADS_IN_FLIGHT
 #define PA_KV_LOADS_IN_FLIGHT 8  // 16-byte K+V loads per lane issued before their use
@@ -58,8 +61,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int kWave = 64;
-constexpr int kWaves = PA_DECODE_WAVES;
-constexpr int kThreads = kWave * kWaves;
+constexpr int kWavesNarrow = PA_DECODE_WAVES;
+constexpr int kWavesWide = PA_DECODE_WAVES_WIDE;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------------
@@ -265,10 +268,10 @@ __device__ __forceinline__ size_t unit_offset(int phys, int u, size_t block_stri
 }
 
 // Fold this wave's units of one (partition, head) into its row state.  The wave
-// owns units first_unit + j * kWaves, j < n_mine; the first n_full are whole.  Lane
-// j of `ids` holds the physical block of the wave's j-th unit (the first kWave of
-// them); a longer list is fetched kWave at a time from the table.
-template <typename T, int D, int BS>
+// owns units first_unit + j * W (W waves per workgroup), j < n_mine; the first n_full
+// are whole.  Lane j of `ids` holds the physical block of the wave's j-th unit (the
+// first kWave of them); a longer list is fetched kWave at a time from the table.
+template <typename T, int D, int BS, int W>
 __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>& st,
                                              const u32x4& q, int ids, const int* table,
                                              int first_unit, const T* k_head, const T* v_head,
@@ -279,7 +282,7 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
   for (int base = 0; base < n_mine; base += kWave) {
     if (base > 0) {
       const int idx = base + lane;
-      ids = idx < n_mine ? table[(first_unit + idx * kWaves) / G::kUnitsPerBlock] : 0;
+      ids = idx < n_mine ? table[(first_unit + idx * W) / G::kUnitsPerBlock] : 0;
     }
     const int chunk_full = min(max(n_full - base, 0), kWave);
     int j = 0;
@@ -290,7 +293,7 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
 #pragma unroll
       for (int u = 0; u < G::kUnroll; ++u) {
         const int phys = __builtin_amdgcn_readlane(ids, j + u);
-        const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j + u) * kWaves, block_stride);
+        const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j + u) * W, block_stride);
         const T* kp = k_head + off + lane_off;
 #pragma unroll
         for (int i = 0; i < G::kLoads; ++i) kr[u][i] = load_kv16(kp + i * G::kTokPerLoad * D);
@@ -298,7 +301,7 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
 #pragma unroll
       for (int u = 0; u < G::kUnroll; ++u) {
         const int phys = __builtin_amdgcn_readlane(ids, j + u);
-        const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j + u) * kWaves, block_stride);
+        const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j + u) * W, block_stride);
         const T* vp = v_head + off + lane_off;
 #pragma unroll
         for (int i = 0; i < G::kLoads; ++i) vr[u][i] = load_kv16(vp + i * G::kTokPerLoad * D);
@@ -312,7 +315,7 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
       u32x4 kr[G::kLoads];
       u32x4 vr[G::kLoads];
       const int phys = __builtin_amdgcn_readlane(ids, j);
-      const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * kWaves, block_stride);
+      const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * W, block_stride);
       const T* kp = k_head + off + lane_off;
       const T* vp = v_head + off + lane_off;
 #pragma unroll
@@ -326,7 +329,7 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
       u32x4 kr[G::kLoads];
       u32x4 vr[G::kLoads];
       const int phys = __builtin_amdgcn_readlane(ids, j);
-      const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * kWaves, block_stride);
+      const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * W, block_stride);
       const T* kp = k_head + off + lane_off;
       const T* vp = v_head + off + lane_off;
 #pragma unroll
@@ -359,13 +362,14 @@ __device__ __forceinline__ void fold_prefix_states(const DecodeParams& prm, int 
 
 // ---------------------------------------------------------------------------------
 // decode, partition pass
-// grid (max partitions, heads, seqs), kThreads threads
+// grid (max partitions, heads, seqs), W wave64s
 // ---------------------------------------------------------------------------------
 
-template <typename T, int D, int BS>
-__global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kernel(DecodeParams prm) {
+template <typename T, int D, int BS, int W>
+__global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kernel(DecodeParams prm) {
   using G = Geometry<T, D, BS>;
   constexpr int kVec = G::kVec;
+  constexpr int kThreads = kWave * W;
 
   const int part = blockIdx.x;
   const int head = blockIdx.y;
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
   // never used), so the K/V stream waits on one dependent load instead of two.
   const int* table = prm.block_tables + static_cast<size_t>(seq) * prm.max_blocks_per_seq;
   const int first_unit = unit_begin + wave;
-  const int blk0 = (first_unit + lane * kWaves) / G::kUnitsPerBlock;
+  const int blk0 = (first_unit + lane * W) / G::kUnitsPerBlock;
   const int ids0 = blk0 < prm.max_blocks_per_seq ? table[blk0] : 0;
   const u32x4 q = load16(static_cast<const T*>(prm.query) +
                          (static_cast<size_t>(seq) * prm.num_heads + head) * D + col_data * kVec);
@@ -415,20 +419,20 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
   const int lane_off = row * D + col_data * kVec;  // element offset of this lane in load 0
   const float scale_log2 = prm.scale * kLog2e;
 
-  // This wave owns units first_unit + j * kWaves, j < n_mine; the last of them may
-  // be partly filled.
+  // This wave owns units first_unit + j * W, j < n_mine; the last of them may be
+  // partly filled.
   const int n_total = unit_end - unit_begin;
-  const int n_mine = n_total > wave ? (n_total - wave + kWaves - 1) / kWaves : 0;
-  const int n_full = full_end - unit_begin > wave ? (full_end - unit_begin - wave + kWaves - 1) / kWaves : 0;
-  const int tail_valid = tok_end - (first_unit + n_full * kWaves) * G::kUnitTok;
+  const int n_mine = n_total > wave ? (n_total - wave + W - 1) / W : 0;
+  const int n_full = full_end - unit_begin > wave ? (full_end - unit_begin - wave + W - 1) / W : 0;
+  const int tail_valid = tok_end - (first_unit + n_full * W) * G::kUnitTok;
 
   RowState<kVec> st;
   st.m = -INFINITY;
   st.l = 0.0f;
 #pragma unroll
   for (int j = 0; j < kVec; ++j) st.acc[j] = 0.0f;
-  attend_units<T, D, BS>(st, q, ids0, table, first_unit, k_head, v_head, block_stride, lane_off, lane,
-                         row, active, n_mine, n_full, tail_valid, scale_log2);
+  attend_units<T, D, BS, W>(st, q, ids0, table, first_unit, k_head, v_head, block_stride, lane_off,
+                            lane, row, active, n_mine, n_full, tail_valid, scale_log2);
 
   // merge the token rows of the wave (lanes with the same col)
 #pragma unroll
@@ -442,9 +446,9 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
   }
 
   // merge the waves through LDS, in wave order
-  __shared__ float s_m[kWaves];
-  __shared__ float s_l[kWaves];
-  __shared__ float s_o[kWaves][D];
+  __shared__ float s_m[W];
+  __shared__ float s_l[W];
+  __shared__ float s_o[W][D];
   if (row == 0 && active) {
 #pragma unroll
     for (int j = 0; j < kVec; ++j) s_o[wave][col * kVec + j] = st.acc[j];
@@ -461,11 +465,11 @@ __global__ __launch_bounds__(kThreads) PA_OCCUPANCY void decode_partitions_kerne
   for (int d = threadIdx.x; d < D; d += kThreads) {
     float m = s_m[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_m[w]);
+    for (int w = 1; w < W; ++w) m = fmaxf(m, s_m[w]);
     float l = 0.0f;
     float o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       const float f = (s_m[w] == -INFINITY) ? 0.0f : fast_exp2(s_m[w] - m);
       l = l + s_l[w] * f;
       o = o + s_o[w][d] * f;
@@ -851,7 +855,13 @@ __global__ __launch_bounds__(256) void block_copy_kernel(CopyParams prm) {
 template <typename T, int D, int BS>
 static hipError_t launch_partitions_t(const DecodeParams& prm, hipStream_t stream) {
   dim3 grid(prm.num_partitions, prm.num_heads, prm.num_seqs);
-  hipLaunchKernelGGL((decode_partitions_kernel<T, D, BS>), grid, dim3(kThreads), 0, stream, prm);
+  if (prm.wide) {
+    hipLaunchKernelGGL((decode_partitions_kernel<T, D, BS, kWavesWide>), grid, dim3(kWave * kWavesWide), 0,
+                       stream, prm);
+  } else {
+    hipLaunchKernelGGL((decode_partitions_kernel<T, D, BS, kWavesNarrow>), grid, dim3(kWave * kWavesNarrow), 0,
+                       stream, prm);
+  }
   return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ struct DecodeParams {
   int32_t slots_per_pair;    // partial-state slots reserved per (seq, head)
   int32_t slot_offset;       // slot of partition 0 of this pass (= prefix slots)
   int32_t prefix_partition_tokens;  // with token_begin: the prefix states' partition length
+  int32_t wide;              // 1: 16 wave64s per workgroup, 0: 8
   float scale;
 };
 

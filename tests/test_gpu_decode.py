@@ -87,6 +87,41 @@ def test_mid_size_matches_oracle(case):
     assert err <= tol_for(dtype), err
 
 
+def unit_tokens(dtype, d, bs):
+    """Tokens one wave folds at once: a block, or 8 loads of 16 bytes per lane with a
+    token row spread over a power of two of lanes."""
+    lanes = 1
+    while lanes < d * np.dtype(dtype).itemsize // 16:
+        lanes *= 2
+    return min(bs, 64 // lanes * 8)
+
+
+WIDE_CASES = [
+    # dtype, D, bs, seqs, heads, ctx range, P: at least 1024 workgroups whose
+    # partitions hold 32 units or more, so the launch uses 16-wave workgroups
+    (np.float16, 128, 16, 32, 32, (1, 1200), 0),
+    (np.float16, 128, 16, 64, 16, (1, 1500), 512),
+    (np.float32, 64, 8, 64, 16, (1, 600), 0),
+    (np.float16, 80, 32, 32, 32, (900, 1100), 0),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES,
+                         ids=lambda c: f"{np.dtype(c[0]).name}-D{c[1]}-bs{c[2]}-S{c[3]}xH{c[4]}-P{c[6]}")
+def test_wide_workgroups_match_oracle(case):
+    from paged_kv_cache_414_amd import ops
+    dtype, d, bs, s, h, (lo, hi), part = case
+    b = workloads.make_static_batch("wide", seed=d + bs + s + hi, num_seqs=s, num_heads=h,
+                                    head_dim=d, block_size=bs, ctx_low=lo, ctx_high=hi,
+                                    dtype=dtype, pool_slack=1.2)
+    p = ops.pa_decode_partition_size(s, h, bs, b.max_context_len, part)
+    n_parts = ops.pa_decode_num_partitions(s, h, bs, b.max_context_len, part)
+    assert s * h * n_parts >= 1024 and p >= 32 * unit_tokens(dtype, d, bs)
+    got = DeviceBatch(b).decode(partition_size=part)
+    assert np.all(np.isfinite(got))
+    assert max_abs_err(got, _oracle(b)) <= tol_for(dtype)
+
+
 # ----------------------------------------------------------------------------------
 # invariants, bit for bit on the GPU
 # ----------------------------------------------------------------------------------

@@ -31,14 +31,14 @@ METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 
 # HBM bytes per launch of the partition pass on this workload (seed 2), from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
-# known-size block copy (FETCH_SIZE x 1.9964, WRITE_SIZE x 1.000); the commands and
+# known-size block copy (FETCH_SIZE x 1.9962, WRITE_SIZE x 1.000); the commands and
 # raw values are in profiles/decode_partitions_llama7b_pmc.md.  Valid only for the
 # kernel source they were taken on.
 MEASURED_TRAFFIC = {
-    "kernel_source_sha256": "07cdc0e722e139c93a0302cddbe9ffc5413a2925dea7ec38300bb28ff7693315",
+    "kernel_source_sha256": "05db3316416328e892c3bc8e3709667ffe93069ffad6390f11da065aaa169a8b",
     "seed": 2,
     "partition_tokens": 2048,
-    "read_bytes": 1934721857,
+    "read_bytes": 1934582707,
     "write_bytes": 786432,
 }
 KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),

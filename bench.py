@@ -162,8 +162,8 @@ def run_mix(cls_name, seed, torch, args, **kw):
     """A step mix, each step one call of the native decode-step executor: wall-clock
     seq-steps/s (host block manager, the per-step staging and the launches included;
     synthetic inputs staged in HBM beforehand) of a second, warm run of the whole mix
-    (the first run is reported beside it); GPU-only seq-steps/s of a third run (HIP
-    events around each step's work, summed); and the last step's decode re-timed alone.
+    (the first run is reported beside it), and the last step's decode re-timed alone
+    (the kernel time of whole steps comes from a rocprofv3 trace of the same runs).
     The same mix driven step by step from Python (the same native block manager and
     kernels, one binding call per operation) is timed the same way."""
     from paged_kv_cache_414_amd import metrics, steps
@@ -183,25 +183,8 @@ def run_mix(cls_name, seed, torch, args, **kw):
         torch.cuda.synchronize()
         return rows / (time.perf_counter() - t0), mix
 
-    def gpu_run(mix):
-        """GPU time of each step: an event pair around each step's enqueued work."""
-        mix._inputs = first._inputs
-        stream = torch.cuda.current_stream()
-        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(mix.steps)]
-        torch.cuda.synchronize()
-        rows = 0
-        for k in range(mix.steps):
-            pairs[k][0].record(stream)
-            rows += mix.run_step(k)
-            pairs[k][1].record(stream)
-        torch.cuda.synchronize()
-        ms = sum(a.elapsed_time(b) for a, b in pairs)
-        return rows / (ms * 1e-3), ms * 1e3 / mix.steps
-
     native_first, _ = wall_run(first)
     native_warm, mix = wall_run(cls(seed=seed, native=True, **kw))
-    gpu_rate, gpu_us = gpu_run(cls(seed=seed, native=True, **kw))
     ms = time_launches(mix.decode_again, 50, torch)
     ctx = mix.last_context_lens()
     kv = mix.kv_bytes(ctx)
@@ -211,8 +194,6 @@ def run_mix(cls_name, seed, torch, args, **kw):
         "steps": mix.steps,
         "seq_steps_per_s_wall": round(native_warm, 1),
         "first_run_seq_steps_per_s_wall": round(native_first, 1),
-        "seq_steps_per_s_gpu": round(gpu_rate, 1),
-        "gpu_us_per_step": round(gpu_us, 2),
         "driver": "native executor, one pa_step_run per step",
         "python_driver_seq_steps_per_s_wall": round(py_warm, 1),
         "python_driver_first_run_seq_steps_per_s_wall": round(py_first, 1),

@@ -33,24 +33,33 @@ METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
 # known-size block copy (FETCH_SIZE x 1.9962, WRITE_SIZE x 1.000); the commands and
 # raw values are in profiles/decode_partitions_llama7b_pmc.md.  Valid only for the
-# kernel source they were taken on.
+# kernel sources they were taken on (sha256 of the kernel file followed by the
+# launch header, whose constants the kernels use).
 MEASURED_TRAFFIC = {
-    "kernel_source_sha256": "05db3316416328e892c3bc8e3709667ffe93069ffad6390f11da065aaa169a8b",
+    "kernel_source_sha256": "to be measured",
     "seed": 2,
     "partition_tokens": 2048,
     "read_bytes": 1934582707,
     "write_bytes": 786432,
 }
-KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                             "paged_kv_cache_414_amd", "csrc", "pa_kernels.hip")
+KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                               "paged_kv_cache_414_amd", "csrc", name)
+                  for name in ("pa_kernels.hip", "pa_launch.h")]
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(seed, partition_tokens):
-    """Counter-measured HBM bytes per launch, or None if the kernel source or the
+    """Counter-measured HBM bytes per launch, or None if the kernel sources or the
     workload differ from the ones the counters were taken on."""
-    import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = kernel_sources_sha256()
     t = MEASURED_TRAFFIC
     if sha != t["kernel_source_sha256"] or seed != t["seed"] or partition_tokens != t["partition_tokens"]:
         return None
@@ -534,6 +543,7 @@ def main():
 
     kv = metrics.decode_kv_bytes(ctx, h_count, d, batch.q.itemsize)
     value = metrics.gbps(kv, ms_step * 1e-3)
+    waves = ops.pa_decode_waves(s_count, h_count, d, bs, max_ctx, args.partition)
     achieved = metrics.gbps(kv, ms_part * 1e-3)
     record = {
         "metric": METRIC,
@@ -564,7 +574,7 @@ def main():
         "decode_launch_ms": decode_spread,
         "kv_bytes_per_step": kv,
         "roofline": {
-            "kernel": "decode_partitions_kernel<f16, 128, 16, 16 waves>",
+            "kernel": f"decode_partitions_kernel<f16, 128, 16>, {waves} waves per workgroup",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": metrics.HBM_PEAK_GBPS,

@@ -118,6 +118,16 @@ int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_heads,
                                  int32_t block_size, int32_t max_context_len,
                                  int32_t partition_size);
 
+/* Wave64s per workgroup the partition pass of pa_decode launches for these
+ * arguments: 16 when each partition holds at least 32 units (the tokens a wave
+ * folds at once: a block, or 8 loads of 16 bytes per lane when the block is
+ * larger) and the launch has at least 1024 (sequence, head, partition)
+ * workgroups, else 8.  The result is the same either way up to floating-point
+ * rounding.  Returns -1 (last error set) for invalid arguments. */
+int32_t pa_decode_waves(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                        int32_t block_size, int32_t max_context_len, int32_t partition_size,
+                        pa_dtype dtype);
+
 /*
  * Bytes of workspace pa_decode needs; 0 when every sequence fits one partition
  * (the workspace pointer may then be NULL).  Layout, with NP =

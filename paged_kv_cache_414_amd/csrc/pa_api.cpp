@@ -138,6 +138,7 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_heads, int32_t block_siz
 constexpr int32_t kWideMinUnits = 32;
 constexpr int64_t kWideMinWorkgroups = 1024;
 
+
 int32_t unit_tokens(pa_dtype dtype, int32_t head_dim, int32_t block_size) {
   const int32_t vec = dtype == PA_F16 ? 8 : 4;  // elements per 16-byte load
   int32_t lanes = 1;                            // lanes per token row: a power of two
@@ -357,6 +358,21 @@ int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_heads, int32_t bl
   const int32_t P = resolve_partition(num_seqs, num_heads, block_size, max_context_len, partition_size);
   if (P < 0) return -1;
   return partitions_for(max_context_len, P);
+}
+
+int32_t pa_decode_waves(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_context_len, int32_t partition_size, pa_dtype dtype) {
+  if (check_dtype_shape(dtype, head_dim, block_size) != PA_OK) return -1;
+  if (num_seqs < 0 || num_heads <= 0) {
+    fail(PA_ERR_INVALID_ARG, "num_seqs %d >= 0 and num_heads %d > 0 required", num_seqs, num_heads);
+    return -1;
+  }
+  const int32_t P = resolve_partition(num_seqs, num_heads, block_size, max_context_len, partition_size);
+  if (P < 0) return -1;
+  const int32_t NP = partitions_for(max_context_len, P);
+  ok();
+  return wide_workgroups(dtype, head_dim, block_size, P, num_seqs, num_heads, NP) ? pa::kDecodeWavesWide
+                                                                                : pa::kDecodeWavesNarrow;
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,

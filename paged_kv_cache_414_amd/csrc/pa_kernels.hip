@@ -36,12 +36,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Build-time tuning knobs (defaults are the measured best on MI355X).
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 8  // wave64s per decode workgroup, short partitions or few workgroups
-#endif
-#ifndef PA_DECODE_WAVES_WIDE
-#define PA_DECODE_WAVES_WIDE 16  // wave64s per decode workgroup otherwise
-#endif
 #ifndef PA_KV_LOADS_IN_FLIGHT
 #define PA_KV_LOADS_IN_FLIGHT 8  // 16-byte K+V loads per lane issued before their use
 #endif
@@ -61,8 +55,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int kWave = 64;
-constexpr int kWavesNarrow = PA_DECODE_WAVES;
-constexpr int kWavesWide = PA_DECODE_WAVES_WIDE;
+constexpr int kWavesNarrow = kDecodeWavesNarrow;  // the two decode workgroup sizes (pa_launch.h)
+constexpr int kWavesWide = kDecodeWavesWide;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------------

@@ -8,6 +8,17 @@
 
 namespace pa {
 
+// Wave64s per workgroup of the decode partition pass: narrow for short partitions or
+// launches of few workgroups, wide otherwise (DecodeParams::wide, chosen on the host).
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 8
+#endif
+#ifndef PA_DECODE_WAVES_WIDE
+#define PA_DECODE_WAVES_WIDE 16
+#endif
+constexpr int kDecodeWavesNarrow = PA_DECODE_WAVES;
+constexpr int kDecodeWavesWide = PA_DECODE_WAVES_WIDE;
+
 struct DecodeParams {
   void* out;
   const void* query;
@@ -27,7 +38,7 @@ struct DecodeParams {
   int32_t slots_per_pair;    // partial-state slots reserved per (seq, head)
   int32_t slot_offset;       // slot of partition 0 of this pass (= prefix slots)
   int32_t prefix_partition_tokens;  // with token_begin: the prefix states' partition length
-  int32_t wide;              // 1: 16 wave64s per workgroup, 0: 8
+  int32_t wide;              // 1: kDecodeWavesWide wave64s per workgroup, 0: kDecodeWavesNarrow
   float scale;
 };
 

@@ -31,6 +31,7 @@ SIGNATURES = {
     "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_num_partitions": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_waves": (_i32, [_i32] * 7),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -161,6 +162,16 @@ def pa_decode_num_partitions(num_seqs, num_heads, block_size, max_context_len,
     if n < 0:
         raise PagedAttentionError(2, lib.pa_last_error().decode())
     return n
+
+
+def pa_decode_waves(num_seqs, num_heads, head_dim, block_size, max_context_len,
+                    partition_size=0, dtype=torch.float16) -> int:
+    """Wave64s per workgroup of pa_decode's partition pass for these arguments."""
+    w = lib.pa_decode_waves(num_seqs, num_heads, head_dim, block_size, max_context_len,
+                            partition_size, _DTYPES[dtype])
+    if w < 0:
+        raise PagedAttentionError(2, lib.pa_last_error().decode())
+    return w
 
 
 def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, block_size, max_context_len,

@@ -157,6 +157,23 @@ def test_shared_prefix_rejects_bad_arguments(ops, over, status):
     assert ops.lib.pa_last_error() != b""
 
 
+def test_decode_workgroup_size_policy(ops):
+    import torch
+    # 16 waves: partitions of 32+ units and 1024+ workgroups; else 8
+    assert ops.pa_decode_waves(96, 32, 128, 16, 2036) == 16     # 3,072 x 128 units
+    assert ops.pa_decode_waves(16, 32, 128, 16, 8192) == 8      # 512 workgroups
+    assert ops.pa_decode_waves(64, 32, 128, 16, 300) == 8       # 19 units per partition
+    assert ops.pa_decode_waves(64, 32, 128, 16, 562) == 16      # 36 units, 2,048 workgroups
+    assert ops.pa_decode_waves(64, 32, 128, 16, 562, 256) == 8  # 16 units per partition
+    # units of 8 tokens (block size 8, fp32 D64: 4 rows per load, 8 loads would be 32 tokens)
+    assert ops.pa_decode_waves(64, 16, 64, 8, 600, 0, torch.float32) == 16
+    # blocks of 256 tokens are walked in units of 32 (fp16 D128: 4 rows per load x 8 loads)
+    assert ops.pa_decode_waves(96, 32, 128, 256, 700) == 8      # P 768: 24 units
+    assert ops.pa_decode_waves(96, 32, 128, 256, 1000) == 16    # P 1024: 32 units
+    with pytest.raises(ops.PagedAttentionError):
+        ops.pa_decode_waves(96, 32, 72, 16, 2036)
+
+
 def test_shared_prefix_planning(ops):
     # an empty batch needs nothing and enqueues nothing
     assert _bad_shared(ops, S=0, out=None, q=None, k=None, v=None, bt=None, ctx=None,

@@ -31,15 +31,15 @@ METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 
 # HBM bytes per launch of the partition pass on this workload (seed 2), from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
-# known-size block copy (FETCH_SIZE x 1.9962, WRITE_SIZE x 1.000); the commands and
+# known-size block copy (FETCH_SIZE x 1.9963, WRITE_SIZE x 1.000); the commands and
 # raw values are in profiles/decode_partitions_llama7b_pmc.md.  Valid only for the
 # kernel sources they were taken on (sha256 of the kernel file followed by the
 # launch header, whose constants the kernels use).
 MEASURED_TRAFFIC = {
-    "kernel_source_sha256": "to be measured",
+    "kernel_source_sha256": "68f35f15166a5839c9b548303292e45bdc2fdc03b40c9523e896037c95aee976",
     "seed": 2,
     "partition_tokens": 2048,
-    "read_bytes": 1934582707,
+    "read_bytes": 1934646259,
     "write_bytes": 786432,
 }
 KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)),

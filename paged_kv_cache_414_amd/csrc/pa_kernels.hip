@@ -533,7 +533,9 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(ReduceParams prm) {
 // matrix products, run on the matrix cores as tiles of 16 tokens x 16 queries:
 //   scores  S^T[t][g] = sum_d K[t][d] Q[g][d]   (v_mfma_f32_16x16x32_f16, A = K tile,
 //           B = Q^T; lane l holds token l%16 of K and query l%16 of Q, both over the
-//           same 8 dims per step: [32c + 8(l/16), +8) at step c)
+//           same 8 dims per step: [32c + 8(l/16), +8) at step c; the K tile is read
+//           as contiguous KiB runs and regrouped into this layout through LDS, so no
+//           load instruction touches 16 rows of 64 bytes)
 //   output  O^T[d][g] = sum_t V[t][d] P[g][t]   (v_mfma_f32_16x16x16_f16, A = V^T,
 //           B = P^T)
 // The matrix-core result layout puts tokens 4(l/16)..+3 of query l%16 in lane l,
@@ -616,9 +618,23 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
   const _Float16* v_head = static_cast<const _Float16*>(prm.value_cache) + static_cast<size_t>(head) * BS * D;
   const float scale_log2 = prm.scale * kLog2e;
 
-  __shared__ float s_m[kPrefixSlots][kTile];
-  __shared__ float s_l[kPrefixSlots][kTile];
-  __shared__ float s_o[kPrefixSlots][kTile][D + 1];  // +1: rows of one lane group hit distinct banks
+  // Each wave's K tile, staged row by row (D + 8 elements per row: the 16 rows one
+  // read instruction touches start on distinct banks); shares its space with the
+  // merge buffers, which are used only after every wave has left the tile loop.
+  constexpr int kKRow = D + 8;
+  union PrefixLds {
+    _Float16 k[kPrefixWaves][kTile * kKRow];
+    struct {
+      float m[kPrefixSlots][kTile];
+      float l[kPrefixSlots][kTile];
+      float o[kPrefixSlots][kTile][D + 1];  // +1: rows of one lane group hit distinct banks
+    } merge;
+  };
+  __shared__ PrefixLds lds;
+  auto& s_m = lds.merge.m;
+  auto& s_l = lds.merge.l;
+  auto& s_o = lds.merge.o;
+  _Float16* s_k = lds.k[wave];
 
   // Tiles qtile, qtile + query_tiles, ...: with query_tiles at least the group size
   // / 16 (the usual case) one tile, every tile of the group in a workgroup of its own.
@@ -642,7 +658,21 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
     for (int dt = 0; dt < kDv; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // Fold one tile (scores, online softmax, value product) into the state.
-    auto fold_tile = [&](const u32x4 (&kv)[kQLoads], const HalfRun<kDv> (&vr)[4]) {
+    auto fold_tile = [&](const u32x4 (&kraw)[kQLoads], const HalfRun<kDv> (&vr)[4]) {
+      // kraw[c] holds elements [512c + 8 lane, +8) of the tile (row-major); regroup
+      // them through this wave's LDS rows into the score product's A layout
+      u32x4 kv[kQLoads];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < kQLoads; ++c) {
+        const int e = 512 * c + 8 * lane;
+        *reinterpret_cast<u32x4*>(s_k + (e / D) * kKRow + e % D) = kraw[c];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < kQLoads; ++c) kv[c] = *reinterpret_cast<const u32x4*>(s_k + c16 * kKRow + 32 * c + 8 * j);
       // scores: sc[v] = <K row 4j+v, query c16>
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -695,15 +725,16 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
                           ? table[(tile_begin + wave + idx * kPrefixWaves) / kTilesPerBlock]
                           : 0;
       const int n_here = min(n_mine - base, kWave);
-      // K row c16 (dims [32c + 8j, +8) per step c) and V rows 4j+v (dims [kDv*c16, +kDv))
-      // of the wave's i-th tile of this chunk
+      // the wave's i-th tile of this chunk: K as 16-byte runs of the row-major tile,
+      // one contiguous KiB per load instruction (regrouped through LDS when folded),
+      // and V rows 4j+v (dims [kDv*c16, +kDv))
       auto load_tile = [&](int i, u32x4 (&kv)[kQLoads], HalfRun<kDv> (&vr)[4]) {
         const int tile = tile_begin + wave + (base + i) * kPrefixWaves;
         const int phys = __builtin_amdgcn_readlane(ids, i);
         const size_t off = static_cast<size_t>(phys) * block_stride +
                            static_cast<size_t>(tile % kTilesPerBlock) * kTile * D;
 #pragma unroll
-        for (int ii = 0; ii < kQLoads; ++ii) kv[ii] = load_kv16(k_head + off + c16 * D + 32 * ii + 8 * j);
+        for (int ii = 0; ii < kQLoads; ++ii) kv[ii] = load_kv16(k_head + off + 512 * ii + 8 * lane);
 #pragma unroll
         for (int v = 0; v < 4; ++v) vr[v].load(v_head + off + (4 * j + v) * D + kDv * c16);
       };
@@ -745,6 +776,7 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
         for (int v = 0; v < 4; ++v) s_o[slot][c16][kDv * (4 * j + v) + dt] = acc[dt][v];
       }
     };
+    __syncthreads();  // every wave is done with its K rows before the merge reuses them
     if constexpr (kPrefixWaves > kPrefixSlots) {
       if (wave >= kPrefixSlots) park(wave - kPrefixSlots);
       __syncthreads();

@@ -287,7 +287,11 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
       admitted_tokens += a->admit_lens[admitted];
       ++admitted;
     }
-    if (admitted > 0) pa_bm_add_sequences(e->bm, a->admit_ids, a->admit_lens, admitted, h + e->off_admit);
+    // the ids were checked unknown and distinct and the blocks counted: this succeeds
+    if (admitted > 0) {
+      st = pa_bm_add_sequences(e->bm, a->admit_ids, a->admit_lens, admitted, h + e->off_admit);
+      if (st != PA_OK) return st;
+    }
   }
 
   // ---- 4. one copy of the staged arrays, by a kernel on the step's stream; with no

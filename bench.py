@@ -336,10 +336,11 @@ def shared_prefix_decode(torch, ops, metrics, args):
 
 
 def graph_step(torch, ops, metrics, args):
-    """Small-batch decode steps (pa_cache_append + pa_decode), launched directly vs
-    replayed from a recorded graph: wall-clock per step over back-to-back steps on
-    fixed inputs (launch overhead isolated)."""
-    from paged_kv_cache_414_amd import graphs, workloads
+    """Small-batch decode steps, launched directly vs replayed from a recorded graph:
+    wall-clock per step over back-to-back steps on fixed inputs (launch overhead
+    isolated), for the two-launch step (pa_cache_append + pa_decode) and for the
+    single pa_decode_append launch."""
+    from paged_kv_cache_414_amd import blocks, graphs, workloads
 
     log(args, "graph-captured step")
     rows = []
@@ -351,12 +352,18 @@ def graph_step(torch, ops, metrics, args):
         k = torch.from_numpy(b.k_pool).cuda()
         v = torch.from_numpy(b.v_pool).cuda()
         g = graphs.DecodeStepGraph(k, v, s_count, 33, 33 * 16, b.scale)
-        g.q.copy_(torch.from_numpy(b.q))
-        g.new_k.copy_(torch.from_numpy(b.q))
-        g.new_v.copy_(torch.from_numpy(b.q))
-        g.block_tables.copy_(torch.from_numpy(b.block_tables))
-        g.context_lens.copy_(torch.from_numpy(b.context_lens))
-        g.slots.fill_(-1)  # time the step without moving the contexts
+        gf = graphs.DecodeStepGraph(k, v, s_count, 33, 33 * 16, b.scale, fused=True)
+        for gg in (g, gf):
+            gg.q.copy_(torch.from_numpy(b.q))
+            gg.new_k.copy_(torch.from_numpy(b.q))
+            gg.new_v.copy_(torch.from_numpy(b.q))
+            gg.block_tables.copy_(torch.from_numpy(b.block_tables))
+            gg.context_lens.copy_(torch.from_numpy(b.context_lens))
+        # the two-launch step appends at the newest position too (the fused one
+        # always does): both rewrite the same slot with the same row every step
+        pos = b.context_lens.astype(np.int64) - 1
+        g.slots.copy_(torch.from_numpy(
+            blocks.slots_for_positions(b.block_tables, pos, 16).astype(np.int32)))
 
         def wall(fn, n=300):
             for _ in range(20):
@@ -371,12 +378,19 @@ def graph_step(torch, ops, metrics, args):
         eager_us = wall(g.run_eager)
         graph_us = wall(g.replay)
         gpu_ms = time_launches(g.replay, 100, torch)
+        fused_us = wall(gf.run_eager)
+        fused_graph_us = wall(gf.replay)
+        fused_gpu_ms = time_launches(gf.run_eager, 100, torch)
         rows.append({"num_seqs": s_count, "sum_context": int(b.context_lens.sum()),
                      "eager_us_per_step": round(eager_us, 2),
                      "graph_us_per_step": round(graph_us, 2),
                      "speedup": round(eager_us / graph_us, 3),
-                     "gpu_us_per_step": round(gpu_ms * 1e3, 2)})
-        del g, k, v
+                     "gpu_us_per_step": round(gpu_ms * 1e3, 2),
+                     "fused_eager_us_per_step": round(fused_us, 2),
+                     "fused_graph_us_per_step": round(fused_graph_us, 2),
+                     "fused_gpu_us_per_step": round(fused_gpu_ms * 1e3, 2),
+                     "fused_speedup": round(eager_us / fused_us, 3)})
+        del g, gf, k, v
         torch.cuda.empty_cache()
     return rows
 

@@ -171,6 +171,32 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_append -- one decode step in one call: each sequence's newest K/V row is
+ * written into its slot and attended to, as the request life cycle orders it ([vLLM
+ * basics] §2.2: the new token's K/V is stored, then attention runs over the context
+ * that counts it).  For every s with L = context_lens[s] >= 1, with t = L - 1,
+ * b = block_tables[s][t / bs] and o = t % bs, and every head h:
+ *     key_cache[b, h, o, :] = new_key[s, h, :];  value_cache[b, h, o, :] = new_value[s, h, :]
+ * then out as pa_decode over the L tokens.  The pools afterwards, and out, are bit for
+ * bit those of pa_cache_append (slot_mapping[s] = b * bs + o) followed by pa_decode
+ * with the same arguments; sequences with L = 0 write nothing.  new_key and new_value:
+ * device [num_seqs, num_heads, head_dim] of the pools' type, 16-byte aligned.  The
+ * appended row is written and read by the workgroup of its own (sequence, head)
+ * alone, so the slot must be read by no other sequence of the call (copy-on-write
+ * carried out before, as pa_cache_append requires distinct slots).  Other arguments,
+ * workspace and errors as pa_decode; the same workspace size.  Saves the separate
+ * append launch, which is most of a step's time at small batch.
+ */
+pa_status pa_decode_append(void* out, const void* query, void* key_cache, void* value_cache,
+                           const void* new_key, const void* new_value,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, float scale, pa_dtype dtype,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * pa_decode_partitions -- first pass of pa_decode alone (same arguments).
  * Sequences with L <= P get their final output written to `out`; for the others,
  * every partition p < ceil(L / P) writes its (m, l, o) state to the workspace and

@@ -458,6 +458,31 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
                           block_size, max_context_len, dtype, partition_size, stream);
 }
 
+pa_status pa_decode_append(void* out, const void* query, void* key_cache, void* value_cache,
+                           const void* new_key, const void* new_value, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan plan;
+  pa_status st = plan_decode(&plan, out, query, key_cache, value_cache, block_tables, context_lens,
+                             num_seqs, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             max_context_len, scale, dtype, partition_size, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (!new_key || !new_value) return fail(PA_ERR_NULL, "new_key and new_value must not be NULL");
+  if (!aligned16(new_key) || !aligned16(new_value))
+    return fail(PA_ERR_INVALID_ARG, "new_key and new_value must be 16-byte aligned");
+  plan.prm.new_key = new_key;
+  plan.prm.new_value = new_value;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = from_hip(pa::launch_decode_partitions(plan.prm, dtype == PA_F16, head_dim, block_size, hs),
+                "decode partition pass launch");
+  if (st != PA_OK) return st;
+  return pa_decode_reduce(out, workspace, workspace_bytes, context_lens, num_seqs, num_heads, head_dim,
+                          block_size, max_context_len, dtype, partition_size, stream);
+}
+
 pa_status pa_cache_append(void* key_cache, void* value_cache, const void* key, const void* value,
                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
                           int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,

@@ -76,6 +76,8 @@ __device__ __forceinline__ u32x4 load_kv16(const void* p) {
 #endif
 }
 
+__device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
 __device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
@@ -261,17 +263,39 @@ __device__ __forceinline__ size_t unit_offset(int phys, int u, size_t block_stri
   return off;
 }
 
+// The newest token's row when the append is fused into the decode (pa_decode_append).
+// `on` only in the workgroup whose partition ends with that token; the wave that owns
+// the partition's last unit reads the row (k, v: this lane's 16 bytes of it) with that
+// unit's loads, folds it from registers, and leaves the lanes of its token row with
+// `store` set and the pool offset `at`: they write it into the pools (k_head, v_head:
+// writable views of the head's chunk of block 0) after the workgroup's last barrier,
+// so no wave ever waits for those stores.
+template <typename T>
+struct NewRow {
+  bool on;
+  const T* k;
+  const T* v;
+  T* k_head;
+  T* v_head;
+  bool store = false;
+  size_t at = 0;
+  u32x4 nk, nv;
+};
+
 // Fold this wave's units of one (partition, head) into its row state.  The wave
 // owns units first_unit + j * W (W waves per workgroup), j < n_mine; the first n_full
 // are whole.  Lane j of `ids` holds the physical block of the wave's j-th unit (the
 // first kWave of them); a longer list is fetched kWave at a time from the table.
+// With nr.on, the partition's last unit is always folded as the partly filled one
+// and its last live token comes from nr (the same bits the append would have stored,
+// so the result is the same as appending first and decoding after).
 template <typename T, int D, int BS, int W>
 __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>& st,
                                              const u32x4& q, int ids, const int* table,
                                              int first_unit, const T* k_head, const T* v_head,
                                              size_t block_stride, int lane_off, int lane,
                                              int row, bool active, int n_mine, int n_full,
-                                             int tail_valid, float scale_log2) {
+                                             int tail_valid, float scale_log2, NewRow<T>& nr) {
   using G = Geometry<T, D, BS>;
   for (int base = 0; base < n_mine; base += kWave) {
     if (base > 0) {
@@ -330,7 +354,30 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
       for (int i = 0; i < G::kLoads; ++i) kr[i] = load_kv16(kp + i * G::kTokPerLoad * D);
 #pragma unroll
       for (int i = 0; i < G::kLoads; ++i) vr[i] = load_kv16(vp + i * G::kTokPerLoad * D);
-      fold_unit<T, D, BS, true>(st, q, kr, vr, scale_log2, row, active, tail_valid);
+      if (nr.on) {
+        // token tail_valid - 1 of this unit is the new one: its registers take the new
+        // row, and the lanes of its row will store it into the pools
+        const int r_new = tail_valid - 1;
+        const int i_new = r_new / G::kTokPerLoad;
+        const bool mine = row == r_new % G::kTokPerLoad;
+        if (mine) {
+          nr.nk = load16(nr.k);
+          nr.nv = load16(nr.v);
+        }
+#pragma unroll
+        for (int i = 0; i < G::kLoads; ++i) {
+          if (i == i_new && mine) {
+            kr[i] = nr.nk;
+            vr[i] = nr.nv;
+          }
+        }
+        nr.store = mine && active;
+        nr.at = off + lane_off + static_cast<size_t>(i_new) * G::kTokPerLoad * D;
+      }
+      if (tail_valid == G::kUnitTok)  // only with nr.on: the new token closes its unit,
+        fold_unit<T, D, BS, false>(st, q, kr, vr, scale_log2, row, active, G::kUnitTok);  // folded whole as without it
+      else
+        fold_unit<T, D, BS, true>(st, q, kr, vr, scale_log2, row, active, tail_valid);
     }
   }
 }
@@ -404,7 +451,15 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
     return;
   }
   const int tok_end = min(ctx, tok_begin + P);
-  const int full_end = tok_end / G::kUnitTok;  // units whose every token is live
+  // pa_decode_append: this partition ends with the newest token (position ctx - 1),
+  // which is read from new_key / new_value and stored into the pools here; its unit
+  // is then folded as a partly filled one (whole or not)
+  NewRow<T> nr;
+  nr.on = prm.new_key != nullptr && tok_end == ctx;
+  const size_t new_at = (static_cast<size_t>(seq) * prm.num_heads + head) * D + col_data * kVec;
+  nr.k = static_cast<const T*>(prm.new_key) + new_at;
+  nr.v = static_cast<const T*>(prm.new_value) + new_at;
+  const int full_end = (nr.on ? tok_end - 1 : tok_end) / G::kUnitTok;  // units folded whole
   const int unit_end = (tok_end + G::kUnitTok - 1) / G::kUnitTok;
 
   const size_t block_stride = static_cast<size_t>(prm.num_heads) * BS * D;  // elements
@@ -412,6 +467,9 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
   const T* v_head = static_cast<const T*>(prm.value_cache) + static_cast<size_t>(head) * BS * D;
   const int lane_off = row * D + col_data * kVec;  // element offset of this lane in load 0
   const float scale_log2 = prm.scale * kLog2e;
+  // the pools are written only by pa_decode_append, whose caller passes them writable
+  nr.k_head = const_cast<T*>(k_head);
+  nr.v_head = const_cast<T*>(v_head);
 
   // This wave owns units first_unit + j * W, j < n_mine; the last of them may be
   // partly filled.
@@ -426,7 +484,7 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
 #pragma unroll
   for (int j = 0; j < kVec; ++j) st.acc[j] = 0.0f;
   attend_units<T, D, BS, W>(st, q, ids0, table, first_unit, k_head, v_head, block_stride, lane_off,
-                            lane, row, active, n_mine, n_full, tail_valid, scale_log2);
+                            lane, row, active, n_mine, n_full, tail_valid, scale_log2, nr);
 
   // merge the token rows of the wave (lanes with the same col)
 #pragma unroll
@@ -480,6 +538,10 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
         prm.ws_l[slot] = l;
       }
     }
+  }
+  if (nr.store) {  // pa_decode_append: the new row into the pools, waited on by no one
+    store16(nr.k_head + nr.at, nr.nk);
+    store16(nr.v_head + nr.at, nr.nv);
   }
 }
 

@@ -40,6 +40,12 @@ struct DecodeParams {
   int32_t prefix_partition_tokens;  // with token_begin: the prefix states' partition length
   int32_t wide;              // 1: kDecodeWavesWide wave64s per workgroup, 0: kDecodeWavesNarrow
   float scale;
+  // pa_decode_append: the row of each sequence's position context_lens[s] - 1 is
+  // taken from new_key / new_value [S, H, D] and also written into the pools at that
+  // position (the pools are then written through key_cache / value_cache); nullptr
+  // for a plain decode.  Only with token_begin == nullptr.
+  const void* new_key = nullptr;
+  const void* new_value = nullptr;
 };
 
 // Prefix pass of the shared-prefix decode: one workgroup per (prefix partition,

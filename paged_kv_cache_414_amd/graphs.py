@@ -13,6 +13,10 @@ staging buffer) and replays.  Two sizes must be fixed at capture: the number of
 sequences (rows of a smaller batch can be retired by a context length of 0 and a
 slot of -1) and an upper bound of the context length, which sizes the decode grid;
 partitions past a sequence's context end at once.
+
+With ``fused=True`` the step is the single launch of pa_decode_append: each row's new
+K/V goes to position context_lens[s] - 1 (a retired row, context 0, writes nothing)
+and ``slots`` is not used.
 """
 
 from __future__ import annotations
@@ -31,13 +35,14 @@ class DecodeStepGraph:
 
     def __init__(self, key_cache: torch.Tensor, value_cache: torch.Tensor, num_seqs: int,
                  max_blocks_per_seq: int, max_context_len: int, scale: float,
-                 partition_size: int = 0):
+                 partition_size: int = 0, fused: bool = False):
         nb, h, bs, d = key_cache.shape
         dev = key_cache.device
         self.k_cache, self.v_cache = key_cache, value_cache
         self.scale = float(scale)
         self.max_context_len = int(max_context_len)
         self.partition_size = int(partition_size)
+        self.fused = bool(fused)
         s = int(num_seqs)
         self.q = torch.zeros((s, h, d), dtype=key_cache.dtype, device=dev)
         self.new_k = torch.zeros_like(self.q)
@@ -63,6 +68,11 @@ class DecodeStepGraph:
             self._enqueue()
 
     def _enqueue(self) -> None:
+        if self.fused:
+            ops.pa_decode_append(self.out, self.q, self.k_cache, self.v_cache, self.new_k,
+                                 self.new_v, self.block_tables, self.context_lens, self.scale,
+                                 self.max_context_len, self.partition_size, self.workspace)
+            return
         ops.pa_cache_append(self.k_cache, self.v_cache, self.new_k, self.new_v, self.slots)
         ops.pa_decode(self.out, self.q, self.k_cache, self.v_cache, self.block_tables,
                       self.context_lens, self.scale, self.max_context_len,

@@ -34,6 +34,8 @@ SIGNATURES = {
     "pa_decode_waves": (_i32, [_i32] * 7),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_append": (_i32, [_vp] * 8 + [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                             _i32, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -220,6 +222,22 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
     _check(lib.pa_decode(*_decode_args(out, query, key_cache, value_cache, block_tables,
                                        context_lens, scale, max_context_len,
                                        partition_size, workspace, stream)))
+    return out
+
+
+def pa_decode_append(out, query, key_cache, value_cache, new_key, new_value, block_tables,
+                     context_lens, scale, max_context_len, partition_size=0, workspace=None,
+                     stream=None):
+    """Append each sequence's newest K/V row ``new_key`` / ``new_value`` [S, H, D] at
+    position context_lens[s] - 1, then paged decode attention into ``out``, in one
+    call (see include/pa.h)."""
+    args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                        max_context_len, partition_size, workspace, stream)
+    _same_device(query, new_key, new_value)
+    for name, t in (("new_key", new_key), ("new_value", new_value)):
+        if t.dtype != query.dtype or t.shape != query.shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {query.dtype} tensor shaped like query")
+    _check(lib.pa_decode_append(*args[:4], _ptr(new_key), _ptr(new_value), *args[4:]))
     return out
 
 

@@ -107,6 +107,38 @@ def test_decode_empty_batch_is_a_no_op(ops):
     assert ops.lib.pa_last_error() == b""
 
 
+def _bad_decode_append(ops, **over):
+    args = dict(out=1 << 20, q=1 << 20, k=1 << 20, v=1 << 20, nk=1 << 20, nv=1 << 20, bt=1 << 20,
+                ctx=1 << 20, S=4, H=4, D=64, bs=16, NB=64, MB=4, maxctx=64, scale=0.125, dtype=0,
+                P=0, ws=None, wsb=0)
+    args.update(over)
+    return ops.lib.pa_decode_append(args["out"], args["q"], args["k"], args["v"], args["nk"],
+                                    args["nv"], args["bt"], args["ctx"], args["S"], args["H"],
+                                    args["D"], args["bs"], args["NB"], args["MB"], args["maxctx"],
+                                    args["scale"], args["dtype"], args["P"], args["ws"],
+                                    args["wsb"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(D=72), 3),
+    (dict(maxctx=65), 2),
+    (dict(P=24), 2),
+    (dict(q=None), 1),
+    (dict(nk=None), 1),
+    (dict(nv=None), 1),
+    (dict(nk=(1 << 20) + 8), 2),   # misaligned new rows
+    (dict(maxctx=64, P=16), 4),
+])
+def test_decode_append_rejects_bad_arguments(ops, over, status):
+    assert _bad_decode_append(ops, **over) == status
+    assert ops.lib.pa_last_error() != b""
+
+
+def test_decode_append_empty_batch_is_a_no_op(ops):
+    assert _bad_decode_append(ops, S=0, out=None, q=None, k=None, v=None, nk=None, nv=None,
+                              bt=None, ctx=None) == 0
+
+
 def test_append_and_copy_reject_bad_arguments(ops):
     lib = ops.lib
     p = 1 << 20

@@ -3,7 +3,9 @@
 Each replay is checked against the same step launched eagerly on a second copy of
 the pool (bit for bit: same kernels, same grid bound) and against the CPU oracle
 (2e-3), with eager work and synchronisation between replays.  Contexts grow by one
-token per replay and one sequence is retired (context 0, slot -1) mid-way."""
+token per replay and one sequence is retired (context 0, slot -1) mid-way.  The
+graph records either the two launches (pa_cache_append, pa_decode) or the single
+pa_decode_append; the eager reference is always the two launches."""
 
 from __future__ import annotations
 
@@ -24,8 +26,9 @@ def _gpu():
         pytest.skip("no GPU")
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_launches", "fused"])
 @pytest.mark.parametrize("partition", [0, 64])
-def test_graph_replays_match_eager_and_oracle(partition):
+def test_graph_replays_match_eager_and_oracle(partition, fused):
     from paged_kv_cache_414_amd import graphs, ops
     b = workloads.make_static_batch("graph", seed=19, num_seqs=6, num_heads=4, head_dim=128,
                                     block_size=16, ctx_low=1, ctx_high=300, dtype=np.float16,
@@ -34,8 +37,8 @@ def test_graph_replays_match_eager_and_oracle(partition):
     k_host, v_host = b.k_pool.copy(), b.v_pool.copy()
     k_a, v_a = dev(b.k_pool), dev(b.v_pool)  # stepped by the graph
     k_b, v_b = dev(b.k_pool), dev(b.v_pool)  # stepped eagerly
-    note(f"capture DecodeStepGraph P={partition}")
-    g = graphs.DecodeStepGraph(k_a, v_a, b.num_seqs, 24, bound, b.scale, partition)
+    note(f"capture DecodeStepGraph P={partition} fused={fused}")
+    g = graphs.DecodeStepGraph(k_a, v_a, b.num_seqs, 24, bound, b.scale, partition, fused=fused)
     out_b = torch.empty_like(g.out)
     ws_b = ops.workspace_for(g.q, k_b, bound, partition)
 

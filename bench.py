@@ -36,10 +36,10 @@ METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 # kernel sources they were taken on (sha256 of the kernel file followed by the
 # launch header, whose constants the kernels use).
 MEASURED_TRAFFIC = {
-    "kernel_source_sha256": "02423172d2920868e4ef7a15a7d4cf72201128e6df4575167d43e711c6bb6d0c",
+    "kernel_source_sha256": "066879b83d09899d5932415f8f38fffa3ab18e7d5c9f27aa83a279d9ec2e3623",
     "seed": 2,
     "partition_tokens": 2048,
-    "read_bytes": 1934840428,
+    "read_bytes": 1934903579,
     "write_bytes": 786432,
 }
 KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)),

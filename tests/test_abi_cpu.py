@@ -248,3 +248,26 @@ def test_swap_rejects_bad_arguments(ops):
     assert lib.pa_swap_blocks(p, None, p, p, p, 2, 4, 64, 16, 8, 8, 0, None) == 1
     assert lib.pa_swap_blocks(p + 4, p, p, p, p, 2, 4, 64, 16, 8, 8, 0, None) == 2
     assert lib.pa_swap_blocks(None, None, None, None, None, 0, 4, 64, 16, 8, 8, 0, None) == 0
+
+
+def test_last_error_is_per_thread(ops):
+    """Threads failing at once each read back their own message (pa_last_error is
+    thread-local; ctypes releases the GIL around the calls)."""
+    import threading
+    dims = [72, 88, 104, 120, 136, 152, 168, 184]
+    bad = []
+
+    def worker(d):
+        for _ in range(400):
+            st = _bad_decode(ops, D=d)
+            msg = ops.lib.pa_last_error().decode()
+            if st != 3 or f"head_dim {d} " not in msg:
+                bad.append((d, st, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=(d,)) for d in dims]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:3]

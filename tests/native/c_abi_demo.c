@@ -2,10 +2,11 @@
  * memory, the host block manager (pa_blocks.h), prompts written with
  * pa_cache_append, a fork that shares a sequence's blocks, one decode step through
  * the executor (pa_step.h, which carries out the copy-on-write, the append and the
- * decode), and the same decode once more through pa_decode (pa.h) with the
- * executor's device tables.  Everything the device computed, and every input, is
- * written to the file named on the command line for a test to check against the
- * oracle.
+ * decode), the same decode once more through pa_decode (pa.h) with the
+ * executor's device tables, and once more through pa_decode_append with the step's
+ * new rows (which rewrites them into the slots they already hold).  Everything the
+ * device computed, and every input, is written to the file named on the command line
+ * for a test to check against the oracle.
  *
  * Build: gcc -std=c11 -D__HIP_PLATFORM_AMD__ -I/opt/rocm/include -Iinclude
  *        c_abi_demo.c -Lpaged_kv_cache_414_amd -lpa -L/opt/rocm/lib -lamdhip64
@@ -15,7 +16,8 @@
  * order: int32 prompt slots [T]; float prompt K, V [T, H, D]; float q, new K, new V
  * [S, H, D]; int32 step slots [S]; int32 copy pairs [C, 2]; int32 block tables
  * [S, MB]; int32 context lengths [S]; float out (executor) [S, H, D]; float out
- * (pa_decode) [S, H, D]; float K pool, V pool [NB, H, BS, D].
+ * (pa_decode) [S, H, D]; float out (pa_decode_append) [S, H, D]; float K pool, V pool
+ * [NB, H, BS, D] after all three.
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -113,9 +115,10 @@ int main(int argc, char** argv) {
   void* d_q = to_device(q, S * row * sizeof(float));
   void* d_nk = to_device(nk, S * row * sizeof(float));
   void* d_nv = to_device(nv, S * row * sizeof(float));
-  void *d_out = NULL, *d_out2 = NULL;
+  void *d_out = NULL, *d_out2 = NULL, *d_out3 = NULL;
   HIP_OK(hipMalloc(&d_out, S * row * sizeof(float)));
   HIP_OK(hipMalloc(&d_out2, S * row * sizeof(float)));
+  HIP_OK(hipMalloc(&d_out3, S * row * sizeof(float)));
   const int64_t running[S] = {0, 1, 2, 3};
   pa_step_args args;
   memset(&args, 0, sizeof(args));
@@ -137,14 +140,20 @@ int main(int argc, char** argv) {
   if (ws_bytes) HIP_OK(hipMalloc(&ws, ws_bytes));
   PA_OK_(pa_decode(d_out2, d_q, kc, vc, view.dev_block_tables, view.dev_context_lens, S, H, D, BS, NB, MB,
                    res.max_context_len, 0.125f, PA_F32, 0, ws, ws_bytes, NULL));
+  /* and through pa_decode_append: the new rows go to position context - 1, where the
+   * executor already put them */
+  PA_OK_(pa_decode_append(d_out3, d_q, kc, vc, d_nk, d_nv, view.dev_block_tables, view.dev_context_lens, S, H,
+                          D, BS, NB, MB, res.max_context_len, 0.125f, PA_F32, 0, ws, ws_bytes, NULL));
   HIP_OK(hipDeviceSynchronize());
 
   float* out = (float*)malloc(S * row * sizeof(float));
   float* out2 = (float*)malloc(S * row * sizeof(float));
+  float* out3 = (float*)malloc(S * row * sizeof(float));
   float* kpool = (float*)malloc(pool_elems * sizeof(float));
   float* vpool = (float*)malloc(pool_elems * sizeof(float));
   HIP_OK(hipMemcpy(out, d_out, S * row * sizeof(float), hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(out2, d_out2, S * row * sizeof(float), hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(out3, d_out3, S * row * sizeof(float), hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(kpool, kc, pool_elems * sizeof(float), hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(vpool, vc, pool_elems * sizeof(float), hipMemcpyDeviceToHost));
 
@@ -164,13 +173,14 @@ int main(int argc, char** argv) {
   put(f, view.context_lens, S * sizeof(int32_t));
   put(f, out, S * row * sizeof(float));
   put(f, out2, S * row * sizeof(float));
+  put(f, out3, S * row * sizeof(float));
   put(f, kpool, pool_elems * sizeof(float));
   put(f, vpool, pool_elems * sizeof(float));
   fclose(f);
 
   pa_step_destroy(eng);
   pa_bm_destroy(bm);
-  void* bufs[] = {kc, vc, d_pk, d_pv, d_slots, d_q, d_nk, d_nv, d_out, d_out2, ws};
+  void* bufs[] = {kc, vc, d_pk, d_pv, d_slots, d_q, d_nk, d_nv, d_out, d_out2, d_out3, ws};
   for (size_t i = 0; i < sizeof(bufs) / sizeof(bufs[0]); ++i) {
     if (bufs[i]) HIP_OK(hipFree(bufs[i]));
   }

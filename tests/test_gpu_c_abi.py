@@ -5,7 +5,8 @@ The demo writes every input it drew and everything the device computed; the orac
 replays the prompts' append, the copy-on-write pairs and the step's append on its
 own zeroed pools, which must then equal the device pools bit for bit, and decodes
 (fp32 KV: max-abs 1e-5).  pa_decode on the executor's tables must reproduce the
-executor's output bit for bit."""
+executor's output bit for bit, and so must pa_decode_append given the step's rows
+again (it rewrites them into the slots the executor put them in)."""
 
 from __future__ import annotations
 
@@ -67,6 +68,7 @@ def _read(path):
     rec["ctx"] = take(np.int32, (s,))
     rec["out"] = take(np.float32, (s, h, d))
     rec["out2"] = take(np.float32, (s, h, d))
+    rec["out3"] = take(np.float32, (s, h, d))
     rec["k_pool"] = take(np.float32, (nb, h, bs, d))
     rec["v_pool"] = take(np.float32, (nb, h, bs, d))
     assert pos == len(raw)
@@ -94,3 +96,4 @@ def test_c_program_matches_oracle(demo, tmp_path):
     want = oracle.decode(r["q"], k, v, r["tables"], r["ctx"], 0.125)
     assert float(np.max(np.abs(r["out"].astype(np.float64) - want))) <= 1e-5
     assert np.array_equal(r["out"].view(np.uint32), r["out2"].view(np.uint32))
+    assert np.array_equal(r["out"].view(np.uint32), r["out3"].view(np.uint32))

@@ -209,3 +209,36 @@ def test_whole_batch_as_one_group():
                                            prefix_blocks_low=16, prefix_blocks_high=16,
                                            suffix_low=1, suffix_high=40)
     assert max_abs_err(run_shared(b), _oracle(b)) <= TOL
+
+
+def _draw_shared_case(i):
+    rng = np.random.default_rng([2026, i])
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64, 128, 256]))
+    n_groups = int(rng.integers(0, 6))
+    sizes = [int(x) for x in rng.integers(1, 40, size=n_groups)]
+    ungrouped = int(rng.integers(0, 4)) if n_groups else int(rng.integers(1, 4))
+    plo = int(rng.integers(0, 4))
+    phi = plo + int(rng.integers(0, max(1, 1024 // bs)))
+    slo = int(rng.integers(0, 200))
+    shi = slo + int(rng.integers(0, 400))
+    unit = max(bs, 16)
+    part = 0 if rng.random() < 0.5 else bs * int(rng.integers(1, max(1, 512 // bs) + 1))
+    ppart = 0 if rng.random() < 0.5 else unit * int(rng.integers(1, max(1, 512 // unit) + 1))
+    mgs = None if rng.random() < 0.5 else 0  # the largest group, or let the library guess
+    return d, bs, sizes, (plo, phi), (slo, shi), ungrouped, part, ppart, mgs
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_shared_prefix_layouts(i):
+    """Seeded random group layouts, block sizes, prefix and suffix lengths, partition
+    lengths of both passes, and max_group_size given or left to the library."""
+    d, bs, sizes, (plo, phi), (slo, shi), ungrouped, part, ppart, mgs = _draw_shared_case(i)
+    b = workloads.make_shared_prefix_batch(f"random{i}", seed=3000 + i, group_sizes=sizes,
+                                           num_heads=2, head_dim=d, block_size=bs,
+                                           prefix_blocks_low=plo, prefix_blocks_high=phi,
+                                           suffix_low=slo, suffix_high=shi, ungrouped=ungrouped,
+                                           pool_slack=1.3)
+    got = run_shared(b, part, ppart, max_group_size=mgs)
+    assert np.all(np.isfinite(got)), i
+    assert max_abs_err(got, _oracle(b)) <= TOL, i

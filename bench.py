@@ -534,6 +534,10 @@ def main():
         ops.pa_cache_append(kc, vc, nk, nv, slots_d)
         ops.pa_decode(out, q, kc, vc, tables, ctx_d, batch.scale, max_ctx, args.partition, ws)
 
+    def fused_step():
+        ops.pa_decode_append(out, q, kc, vc, nk, nv, tables, ctx_d, batch.scale, max_ctx,
+                             args.partition, ws)
+
     def partitions_only():
         ops.pa_decode_partitions(out, q, kc, vc, tables, ctx_d, batch.scale, max_ctx,
                                  args.partition, ws)
@@ -553,6 +557,7 @@ def main():
         partitions_only()
     ms_part = time_launches(partitions_only, args.steps, torch)
     ms_decode = time_launches(decode_only, args.steps, torch)
+    ms_fused = time_launches(fused_step, args.steps, torch)
     decode_spread = launch_spread(decode_only, args.steps, torch)
 
     kv = metrics.decode_kv_bytes(ctx, h_count, d, batch.q.itemsize)
@@ -586,6 +591,9 @@ def main():
         "decode_ms": round(ms_decode, 5),
         "decode_kv_gbps": round(metrics.gbps(kv, ms_decode * 1e-3), 2),
         "decode_launch_ms": decode_spread,
+        "fused_step": {"call": "pa_decode_append (the same append and decode in one launch)",
+                       "ms": round(ms_fused, 5),
+                       "kv_gbps": round(metrics.gbps(kv, ms_fused * 1e-3), 2)},
         "kv_bytes_per_step": kv,
         "roofline": {
             "kernel": f"decode_partitions_kernel<f16, 128, 16>, {waves} waves per workgroup",

@@ -31,15 +31,15 @@ METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 
 # HBM bytes per launch of the partition pass on this workload (seed 2), from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
-# known-size block copy (FETCH_SIZE x 1.9963, WRITE_SIZE x 1.000); the commands and
+# known-size block copy (FETCH_SIZE x 1.9987, WRITE_SIZE x 1.000); the commands and
 # raw values are in profiles/decode_partitions_llama7b_pmc.md.  Valid only for the
 # kernel sources they were taken on (sha256 of the kernel file followed by the
 # launch header, whose constants the kernels use).
 MEASURED_TRAFFIC = {
-    "kernel_source_sha256": "066879b83d09899d5932415f8f38fffa3ab18e7d5c9f27aa83a279d9ec2e3623",
+    "kernel_source_sha256": "31651b5448c86739cf567b704c365d20305ba4570e1aac8f2e45db89e4ca22dd",
     "seed": 2,
     "partition_tokens": 2048,
-    "read_bytes": 1934903579,
+    "read_bytes": 1937339043,
     "write_bytes": 786432,
 }
 KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -421,6 +421,63 @@ def swap_throughput(torch, ops, args, pairs=2048):
     return res
 
 
+def append_copy_throughput(torch, ops, metrics, args):
+    """pa_cache_append and pa_block_copy alone, Llama-shaped rows and blocks (32 heads
+    x 128, block 16, fp16), on the GPU pool: average time per launch over back-to-back
+    launches and bytes read + written per second against HBM peak.
+
+    append: the 96 rows of one decode step (latency-sized), and 4,096 prompt rows
+    filling 256 whole blocks scattered over the pool (bandwidth-sized).  copy: the 56
+    copy-on-write pairs of the shared-prefix step (8 groups x 7 copies), and 2,048
+    pairs (512 MiB of K and V read and written)."""
+    log(args, "append and block copy")
+    heads, bs, d = 32, 16, 128
+    nb = 8192
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    kc = torch.randn((nb, heads, bs, d), dtype=torch.float16, device="cuda", generator=gen)
+    vc = torch.randn((nb, heads, bs, d), dtype=torch.float16, device="cuda", generator=gen)
+    rng = np.random.default_rng([args.seed, 11])
+    ids = rng.permutation(nb).astype(np.int64)
+    n = max(50, args.steps)
+    res = {}
+    for name, tokens in (("append_step_rows", 96), ("append_prompt_rows", 4096)):
+        if tokens <= 96:  # one row at the end of each of 96 blocks
+            slots = ids[:tokens] * bs + (bs - 1)
+        else:             # whole blocks, token t at offset t % bs of block t // bs
+            t = np.arange(tokens)
+            slots = ids[t // bs] * bs + t % bs
+        slots_d = torch.from_numpy(slots.astype(np.int32)).cuda()
+        nk = torch.randn((tokens, heads, d), dtype=torch.float16, device="cuda", generator=gen)
+        nv = torch.randn((tokens, heads, d), dtype=torch.float16, device="cuda", generator=gen)
+        fn = lambda: ops.pa_cache_append(kc, vc, nk, nv, slots_d)  # noqa: E731
+        for _ in range(10):
+            fn()
+        ms = time_launches(fn, n, torch)
+        moved = metrics.append_bytes(tokens, heads, d, 2)
+        res[name] = {"rows": tokens, "us": round(ms * 1e3, 2), "bytes": moved,
+                     "gbps": round(metrics.gbps(moved, ms * 1e-3), 1),
+                     "pct_of_hbm_peak": round(100.0 * metrics.gbps(moved, ms * 1e-3) /
+                                              metrics.HBM_PEAK_GBPS, 1)}
+    for name, pairs in (("copy_on_write_pairs", 56), ("copy_large", 2048)):
+        src = ids[:pairs]
+        dst = ids[nb - pairs:]
+        pairs_d = torch.from_numpy(np.stack([src, dst], axis=1).astype(np.int32)).cuda()
+        fn = lambda: ops.pa_block_copy(kc, vc, pairs_d)  # noqa: E731
+        for _ in range(5):
+            fn()
+        ms = time_launches(fn, n if pairs < 1024 else 20, torch)
+        moved = metrics.block_copy_bytes(pairs, heads, bs, d, 2)
+        res[name] = {"pairs": pairs, "us": round(ms * 1e3, 2), "bytes": moved,
+                     "gbps": round(metrics.gbps(moved, ms * 1e-3), 1),
+                     "pct_of_hbm_peak": round(100.0 * metrics.gbps(moved, ms * 1e-3) /
+                                              metrics.HBM_PEAK_GBPS, 1)}
+    res["note"] = ("bytes = K and V rows read plus written; the step rows and the 56 pairs "
+                   "are latency-sized (a few MB), so their GB/s is not a bandwidth figure")
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
 def shared_prefix_groups(torch, ops, metrics, args):
     """pa_decode against pa_decode_shared_prefix for other group layouts (32 heads x
     128, block 16, fp16; each member holds 200-330 tokens of its own after the shared
@@ -615,6 +672,7 @@ def main():
         if args.graph:
             record["graph_step"] = graph_step(torch, ops, metrics, args)
         record["block_swap"] = swap_throughput(torch, ops, args)
+        record["append_and_copy"] = append_copy_throughput(torch, ops, metrics, args)
     if args.mixes:
         record["step_mixes"] = {
             "continuous_batching": run_mix("ContinuousBatching", 3, torch, args),

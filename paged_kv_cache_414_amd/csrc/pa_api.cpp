@@ -495,9 +495,8 @@ pa_status pa_cache_append(void* key_cache, void* value_cache, const void* key, c
   if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size exceeds the int32 slot range");
   const int32_t row_bytes = head_dim * static_cast<int32_t>(elem_bytes(dtype));
-  const int64_t threads = static_cast<int64_t>(num_tokens) * num_heads * (row_bytes / 16);
-  if ((threads + 255) / 256 > INT32_MAX)
-    return fail(PA_ERR_INVALID_ARG, "num_tokens * num_heads too large for one launch");
+  if (static_cast<int64_t>(num_heads) * (row_bytes / 16) > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_heads * head_dim too large for one launch");
   if (num_tokens == 0) return ok();
   if (!key_cache || !value_cache || !key || !value || !slot_mapping)
     return fail(PA_ERR_NULL, "a required pointer is NULL (key_cache, value_cache, key, value, slot_mapping)");

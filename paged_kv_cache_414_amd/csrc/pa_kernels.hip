@@ -890,56 +890,6 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
 }
 
 // ---------------------------------------------------------------------------------
-// cache append: one thread per 16 bytes of a (token, head) row, K and V
-// ---------------------------------------------------------------------------------
-
-__global__ __launch_bounds__(256) void cache_append_kernel(AppendParams prm) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int chunks = prm.row_bytes / 16;
-  const int64_t total = static_cast<int64_t>(prm.num_tokens) * prm.num_heads * chunks;
-  if (idx >= total) return;
-  const int c = static_cast<int>(idx % chunks);
-  const int64_t th = idx / chunks;  // token * heads + head
-  const int h = static_cast<int>(th % prm.num_heads);
-  const int i = static_cast<int>(th / prm.num_heads);
-  const int slot = prm.slot_mapping[i];
-  if (slot < 0) return;
-  const int b = slot / prm.block_size;
-  const int o = slot % prm.block_size;
-  const size_t dst = ((static_cast<size_t>(b) * prm.num_heads + h) * prm.block_size + o) *
-                         static_cast<size_t>(prm.row_bytes) + static_cast<size_t>(c) * 16;
-  const size_t src = static_cast<size_t>(th) * prm.row_bytes + static_cast<size_t>(c) * 16;
-  const u32x4 kv = load16(static_cast<const char*>(prm.key) + src);
-  const u32x4 vv = load16(static_cast<const char*>(prm.value) + src);
-  *reinterpret_cast<u32x4*>(static_cast<char*>(prm.key_cache) + dst) = kv;
-  *reinterpret_cast<u32x4*>(static_cast<char*>(prm.value_cache) + dst) = vv;
-}
-
-// ---------------------------------------------------------------------------------
-// block copy between pools (the same pool for copy-on-write, the GPU pool and a
-// pinned host pool for swapping): grid (pairs, chunk groups of a block); 16 bytes
-// per thread per step
-// ---------------------------------------------------------------------------------
-
-__global__ __launch_bounds__(256) void block_copy_kernel(CopyParams prm) {
-  const int pair = blockIdx.x;
-  const int src = prm.block_pairs[2 * pair];
-  const int dst = prm.block_pairs[2 * pair + 1];
-  const int64_t chunks = prm.block_bytes / 16;
-  const char* ks = static_cast<const char*>(prm.src_key) + static_cast<size_t>(src) * prm.block_bytes;
-  const char* vs = static_cast<const char*>(prm.src_value) + static_cast<size_t>(src) * prm.block_bytes;
-  char* kd = static_cast<char*>(prm.dst_key) + static_cast<size_t>(dst) * prm.block_bytes;
-  char* vd = static_cast<char*>(prm.dst_value) + static_cast<size_t>(dst) * prm.block_bytes;
-  for (int64_t c = static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x; c < chunks;
-       c += static_cast<int64_t>(gridDim.y) * blockDim.x) {
-    const u32x4 k = load16(ks + c * 16);
-    const u32x4 v = load16(vs + c * 16);
-    *reinterpret_cast<u32x4*>(kd + c * 16) = k;
-    *reinterpret_cast<u32x4*>(vd + c * 16) = v;
-  }
-}
-
-// ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
 
@@ -1044,23 +994,6 @@ hipError_t launch_decode_prefix(const PrefixParams& prm, int head_dim, int block
     case 128: return launch_prefix_d<128>(prm, block_size, stream);
     default: return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_cache_append(const AppendParams& prm, hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(prm.num_tokens) * prm.num_heads * (prm.row_bytes / 16);
-  const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(cache_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, prm);
-  return hipGetLastError();
-}
-
-hipError_t launch_block_copy(const CopyParams& prm, hipStream_t stream) {
-  const int64_t chunks = prm.block_bytes / 16;
-  int64_t gy = (chunks + 256 * 4 - 1) / (256 * 4);  // about 4 chunks per thread
-  if (gy < 1) gy = 1;
-  if (gy > 1024) gy = 1024;
-  hipLaunchKernelGGL(block_copy_kernel, dim3(prm.num_pairs, static_cast<unsigned>(gy)), dim3(256), 0,
-                     stream, prm);
-  return hipGetLastError();
 }
 
 }  // namespace pa

@@ -1,5 +1,6 @@
 // Internal interface between the C ABI (pa_api.cpp) and the HIP kernels
-// (pa_kernels.hip).  Arguments here are already validated.
+// (pa_kernels.hip: decode; pa_copy.hip: append and block copy).  Arguments here
+// are already validated.
 #ifndef PA_LAUNCH_H_
 #define PA_LAUNCH_H_
 

@@ -51,6 +51,27 @@ def test_cache_append_bit_exact(case, num_tokens):
     assert np.array_equal(_bits(vd.cpu().numpy()), _bits(ev))
 
 
+def test_cache_append_more_tokens_than_one_grid_column():
+    """70,000 rows: more than the 65,535 tokens one launch column holds, so workgroups
+    walk several tokens each."""
+    from paged_kv_cache_414_amd import ops
+    rng = np.random.default_rng(65536)
+    h, bs, d, nb, num_tokens = 2, 16, 64, 5000, 70000
+    k_pool = workloads.normal(rng, (nb, h, bs, d), np.float16)
+    v_pool = workloads.normal(rng, (nb, h, bs, d), np.float16)
+    key = workloads.normal(rng, (num_tokens, h, d), np.float16)
+    value = workloads.normal(rng, (num_tokens, h, d), np.float16)
+    slots = rng.choice(nb * bs, size=num_tokens, replace=False).astype(np.int32)
+    slots[rng.random(num_tokens) < 0.05] = -1
+    kd, vd = dev(k_pool), dev(v_pool)
+    note(f"pa_cache_append T={num_tokens} H={h} D={d} bs={bs}")
+    ops.pa_cache_append(kd, vd, dev(key), dev(value), dev(slots))
+    torch.cuda.synchronize()
+    ek, ev = oracle.cache_append(k_pool, v_pool, key, value, slots)
+    assert np.array_equal(_bits(kd.cpu().numpy()), _bits(ek))
+    assert np.array_equal(_bits(vd.cpu().numpy()), _bits(ev))
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{np.dtype(c[0]).name}-D{c[1]}-bs{c[2]}-H{c[3]}")
 @pytest.mark.parametrize("num_pairs", [1, 56, 200])
 def test_block_copy_bit_exact(case, num_pairs):

@@ -64,22 +64,60 @@ def _split_points(length, cuts):
     return list(zip(pts[:-1], pts[1:]))
 
 
-def test_lse_merge_equals_unsplit(tiny_batches):
-    """Merging partition states by log-sum-exp gives back the unsplit attention."""
-    for batch in tiny_batches:
-        full = oracle.decode(batch.q, batch.k_pool, batch.v_pool, batch.block_tables,
-                             batch.context_lens, batch.scale)
+def _pin_lse_merge(state_fn, merge_fn, batches):
+    """Merging partition states by log-sum-exp gives back the unsplit attention
+    (the brute-force scalar decode, not the oracle's own decode)."""
+    for batch in batches:
+        full = oracle.brute_force_decode(batch.q, batch.k_pool, batch.v_pool,
+                                         batch.block_tables, batch.context_lens, batch.scale)
         for s in range(batch.num_seqs):
             length = int(batch.context_lens[s])
             for cuts in ([16], [7, 33], [1, 2, 3, 40], list(range(16, 64, 16))):
                 parts = _split_points(length, cuts)
                 for h in range(batch.num_heads):
-                    st = [oracle.partition_state(batch.q[s, h], batch.k_pool,
-                                                 batch.v_pool, batch.block_tables[s],
-                                                 length, h, batch.scale, a, b)
+                    st = [state_fn(batch.q[s, h], batch.k_pool, batch.v_pool,
+                                   batch.block_tables[s], length, h, batch.scale, a, b)
                           for a, b in parts]
-                    merged = oracle.merge_partition_states(*zip(*st))
+                    merged = merge_fn(*zip(*st))
                     np.testing.assert_allclose(merged, full[s, h], rtol=0, atol=1e-12)
+
+
+def test_lse_merge_equals_unsplit(tiny_batches):
+    _pin_lse_merge(oracle.partition_state, oracle.merge_partition_states, tiny_batches)
+
+
+def _merge_without_rescaled_sums(ms, ls, os_):
+    ms, ls, os_ = (np.asarray(x, dtype=np.float64) for x in (ms, ls, os_))
+    f = np.exp(ms - ms.max())
+    return (f[:, None] * os_).sum(axis=0) / ls.sum()
+
+
+def _merge_by_averaging(ms, ls, os_):
+    os_ = np.asarray(os_, dtype=np.float64)
+    return (os_ / np.asarray(ls, dtype=np.float64)[:, None]).mean(axis=0)
+
+
+def _merge_wrong_sign(ms, ls, os_):
+    ms, ls, os_ = (np.asarray(x, dtype=np.float64) for x in (ms, ls, os_))
+    f = np.exp(ms.max() - ms)
+    return (f[:, None] * os_).sum(axis=0) / (f * ls).sum()
+
+
+def _state_skipping_first_token(q_row, k_pool, v_pool, row, length, head, scale, start, stop):
+    if min(stop, length) - start > 1:
+        start += 1
+    return oracle.partition_state(q_row, k_pool, v_pool, row, length, head, scale, start, stop)
+
+
+@pytest.mark.parametrize("state_fn, merge_fn", [
+    (oracle.partition_state, _merge_without_rescaled_sums),
+    (oracle.partition_state, _merge_by_averaging),
+    (oracle.partition_state, _merge_wrong_sign),
+    (_state_skipping_first_token, oracle.merge_partition_states),
+], ids=["unscaled-sums", "average", "wrong-sign", "skip-first-token"])
+def test_planted_merge_mistake_is_caught(state_fn, merge_fn, tiny_batches):
+    with pytest.raises(AssertionError):
+        _pin_lse_merge(state_fn, merge_fn, tiny_batches[:1])
 
 
 def test_partition_state_definition():

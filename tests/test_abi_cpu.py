@@ -146,6 +146,8 @@ def test_append_and_copy_reject_bad_arguments(ops):
     assert lib.pa_cache_append(p, p, p, None, p, 4, 4, 64, 16, 64, 0, None) == 1
     assert lib.pa_cache_append(p, p, p, p, p, -1, 4, 64, 16, 64, 0, None) == 2
     assert lib.pa_cache_append(None, None, None, None, None, 0, 4, 64, 16, 64, 0, None) == 0
+    # heads x 16-byte chunks of a row must fit the launch's int32 row index
+    assert lib.pa_cache_append(p, p, p, p, p, 4, 1 << 30, 64, 16, 64, 1, None) == 2
     assert lib.pa_block_copy(p, p, p, 2, 4, 72, 16, 64, 0, None) == 3
     assert lib.pa_block_copy(p, p, p, 2, 4, 64, 24, 64, 0, None) == 3
     assert lib.pa_block_copy(p, None, p, 2, 4, 64, 16, 64, 0, None) == 1

@@ -332,6 +332,19 @@ def test_many_sequences_with_empty_and_tiny_contexts():
     assert max_abs_err(got, want) <= 2e-3
 
 
+def test_most_sequences_one_launch_holds():
+    """65,535 sequences, the grid's z limit (one more is refused on the host),
+    contexts 0 to 3 tokens."""
+    b = workloads.make_static_batch("max_seqs", seed=43, num_seqs=65535, num_heads=1, head_dim=64,
+                                    block_size=16, ctx_low=0, ctx_high=3, dtype=np.float16,
+                                    pool_slack=1.1)
+    note("pa_decode with 65,535 sequences")
+    got = DeviceBatch(b).decode()
+    want = _oracle(b)
+    assert np.all(got[b.context_lens == 0] == 0)
+    assert max_abs_err(got, want) <= 2e-3
+
+
 def test_blocks_beyond_4_gib_offsets():
     """Blocks placed past the 4 GiB byte offset of a 10 GB device pool (64-bit
     addressing); the oracle runs on a compact copy with renumbered blocks."""

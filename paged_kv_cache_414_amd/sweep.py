@@ -8,7 +8,8 @@ sequences, contexts uniform in [300, 2048], fp16): for every block size it repor
 the decode time and KV GB/s, the padding waste of the last blocks, the block-table
 entries per sequence, and the host block manager's time to reserve one token per
 sequence (one decode step's bookkeeping).  A second sweep varies the head dim at
-block size 16 (32 heads).
+block size 16 (32 heads), and a third fp32 K/V and q against fp16 (block size 16,
+32 heads x 128).
 
 Inputs: the contexts and the scattered block ids are drawn with numpy (PCG64,
 seeded); the K/V pools, which only need to exist for timing, are filled on the GPU
@@ -46,7 +47,7 @@ def _time(fn, n: int) -> float:
 
 
 def _case(seed: int, ctx: np.ndarray, num_heads: int, head_dim: int, block_size: int,
-          steps: int) -> dict:
+          steps: int, dtype: torch.dtype = torch.float16) -> dict:
     rng = np.random.default_rng([seed, block_size, head_dim])
     n_blk = -(-ctx.astype(np.int64) // block_size)
     needed = int(n_blk.sum())
@@ -61,9 +62,9 @@ def _case(seed: int, ctx: np.ndarray, num_heads: int, head_dim: int, block_size:
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed * 1000 + block_size + head_dim)
     shape = (num_blocks, num_heads, block_size, head_dim)
-    k = torch.randn(shape, dtype=torch.float16, device="cuda", generator=gen)
-    v = torch.randn(shape, dtype=torch.float16, device="cuda", generator=gen)
-    q = torch.randn((ctx.size, num_heads, head_dim), dtype=torch.float16, device="cuda",
+    k = torch.randn(shape, dtype=dtype, device="cuda", generator=gen)
+    v = torch.randn(shape, dtype=dtype, device="cuda", generator=gen)
+    q = torch.randn((ctx.size, num_heads, head_dim), dtype=dtype, device="cuda",
                     generator=gen)
     out = torch.empty_like(q)
     tables_d = torch.from_numpy(tables).cuda()
@@ -72,7 +73,7 @@ def _case(seed: int, ctx: np.ndarray, num_heads: int, head_dim: int, block_size:
     ws = ops.workspace_for(q, k, max_ctx, 0)
     ms = _time(lambda: ops.pa_decode(out, q, k, v, tables_d, ctx_d, 1.0 / np.sqrt(head_dim),
                                      max_ctx, 0, ws), steps)
-    kv = metrics.decode_kv_bytes(ctx, num_heads, head_dim, 2)
+    kv = metrics.decode_kv_bytes(ctx, num_heads, head_dim, q.element_size())
     del k, v, q, out, ws
     torch.cuda.empty_cache()
     allocated = int(n_blk.sum()) * block_size
@@ -89,6 +90,7 @@ def _case(seed: int, ctx: np.ndarray, num_heads: int, head_dim: int, block_size:
     host_us = (time.perf_counter() - t0) / rounds * 1e6
     return {
         "block_size": block_size, "head_dim": head_dim, "num_heads": num_heads,
+        "dtype": "f32" if dtype == torch.float32 else "f16",
         "partition_tokens": ops.pa_decode_partition_size(ctx.size, num_heads, block_size, max_ctx),
         "decode_ms": round(ms, 5),
         "kv_gbps": round(metrics.gbps(kv, ms * 1e-3), 1),
@@ -104,12 +106,16 @@ def run(seed: int = 2, steps: int = 50) -> dict:
     ctx = rng.integers(300, 2049, size=96).astype(np.int32)
     by_block = [_case(seed, ctx, 32, 128, bs, steps) for bs in BLOCK_SIZES]
     by_dim = [_case(seed, ctx, 32, d, 16, steps) for d in HEAD_DIMS]
+    by_dtype = [_case(seed, ctx, 32, 128, 16, steps, dtype)
+                for dtype in (torch.float16, torch.float32)]
     return {
         "metric": "pa_decode KV GB/s by block size and head dim (1 GPU)",
-        "workload": "96 seqs, contexts U[300, 2048], fp16 K/V and q, fp32 accumulate",
+        "workload": "96 seqs, contexts U[300, 2048], fp16 K/V and q (fp32 in the dtype "
+                    "sweep), fp32 accumulate",
         "sum_context": int(ctx.sum()),
         "block_size_sweep": by_block,
         "head_dim_sweep": by_dim,
+        "dtype_sweep": by_dtype,
         "host_step_us_note": "native block manager: reserve 96 slots + build the block "
                              "tables, per step, on the host",
     }

@@ -427,9 +427,11 @@ def append_copy_throughput(torch, ops, metrics, args):
     launches and bytes read + written per second against HBM peak.
 
     append: the 96 rows of one decode step (latency-sized), and 4,096 prompt rows
-    filling 256 whole blocks scattered over the pool (bandwidth-sized).  copy: the 56
-    copy-on-write pairs of the shared-prefix step (8 groups x 7 copies), and 2,048
-    pairs (512 MiB of K and V read and written)."""
+    filling 256 whole blocks scattered over the pool (bandwidth-sized; the launches
+    cycle through 6 sets of rows and blocks, 400 MB in all, so that no launch finds the
+    previous one's rows in the 256 MB Infinity Cache).  copy: the 56 copy-on-write
+    pairs of the shared-prefix step (8 groups x 7 copies), and 2,048 pairs (512 MiB of
+    K and V read and written)."""
     log(args, "append and block copy")
     heads, bs, d = 32, 16, 128
     nb = 8192
@@ -440,16 +442,25 @@ def append_copy_throughput(torch, ops, metrics, args):
     ids = rng.permutation(nb).astype(np.int64)
     n = max(50, args.steps)
     res = {}
-    for name, tokens in (("append_step_rows", 96), ("append_prompt_rows", 4096)):
-        if tokens <= 96:  # one row at the end of each of 96 blocks
-            slots = ids[:tokens] * bs + (bs - 1)
-        else:             # whole blocks, token t at offset t % bs of block t // bs
-            t = np.arange(tokens)
-            slots = ids[t // bs] * bs + t % bs
-        slots_d = torch.from_numpy(slots.astype(np.int32)).cuda()
-        nk = torch.randn((tokens, heads, d), dtype=torch.float16, device="cuda", generator=gen)
-        nv = torch.randn((tokens, heads, d), dtype=torch.float16, device="cuda", generator=gen)
-        fn = lambda: ops.pa_cache_append(kc, vc, nk, nv, slots_d)  # noqa: E731
+    for name, tokens, sets in (("append_step_rows", 96, 1), ("append_prompt_rows", 4096, 6)):
+        args_of_set = []
+        for j in range(sets):
+            if tokens <= 96:  # one row at the end of each of 96 blocks
+                slots = ids[:tokens] * bs + (bs - 1)
+            else:             # whole blocks, token t at offset t % bs of block t // bs
+                t = np.arange(tokens)
+                slots = ids[j * (tokens // bs) + t // bs] * bs + t % bs
+            slots_d = torch.from_numpy(slots.astype(np.int32)).cuda()
+            nk = torch.randn((tokens, heads, d), dtype=torch.float16, device="cuda", generator=gen)
+            nv = torch.randn((tokens, heads, d), dtype=torch.float16, device="cuda", generator=gen)
+            args_of_set.append((nk, nv, slots_d))
+        turn = [0]
+
+        def fn():
+            nk, nv, slots_d = args_of_set[turn[0] % sets]
+            turn[0] += 1
+            ops.pa_cache_append(kc, vc, nk, nv, slots_d)
+
         for _ in range(10):
             fn()
         ms = time_launches(fn, n, torch)

@@ -181,11 +181,13 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
  * bit those of pa_cache_append (slot_mapping[s] = b * bs + o) followed by pa_decode
  * with the same arguments; sequences with L = 0 write nothing.  new_key and new_value:
  * device [num_seqs, num_heads, head_dim] of the pools' type, 16-byte aligned.  The
- * appended row is written and read by the workgroup of its own (sequence, head)
- * alone, so the slot must be read by no other sequence of the call (copy-on-write
- * carried out before, as pa_cache_append requires distinct slots).  Other arguments,
- * workspace and errors as pa_decode; the same workspace size.  Saves the separate
- * append launch, which is most of a step's time at small batch.
+ * attention takes the new row from new_key / new_value; one extra workgroup per
+ * sequence stores it into the pools while the attention runs, so the slot must be
+ * read by no other sequence of the call (copy-on-write carried out before, as
+ * pa_cache_append requires distinct slots).  num_heads must be below 65535 (the extra
+ * workgroups take one more grid row).  Other arguments, workspace and errors as
+ * pa_decode; the same workspace size.  Saves the separate append launch, which is
+ * most of a step's time at small batch.
  */
 pa_status pa_decode_append(void* out, const void* query, void* key_cache, void* value_cache,
                            const void* new_key, const void* new_value,

@@ -266,19 +266,13 @@ __device__ __forceinline__ size_t unit_offset(int phys, int u, size_t block_stri
 // The newest token's row when the append is fused into the decode (pa_decode_append).
 // `on` only in the workgroup whose partition ends with that token; the wave that owns
 // the partition's last unit reads the row (k, v: this lane's 16 bytes of it) with that
-// unit's loads, folds it from registers, and leaves the lanes of its token row with
-// `store` set and the pool offset `at`: they write it into the pools (k_head, v_head:
-// writable views of the head's chunk of block 0) after the workgroup's last barrier,
-// so no wave ever waits for those stores.
+// unit's loads and folds it from registers.  The row reaches the pools through a
+// workgroup of its own (store_new_row), so no decode workgroup waits on a store.
 template <typename T>
 struct NewRow {
   bool on;
   const T* k;
   const T* v;
-  T* k_head;
-  T* v_head;
-  bool store = false;
-  size_t at = 0;
   u32x4 nk, nv;
 };
 
@@ -371,8 +365,6 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
             vr[i] = nr.nv;
           }
         }
-        nr.store = mine && active;
-        nr.at = off + lane_off + static_cast<size_t>(i_new) * G::kTokPerLoad * D;
       }
       if (tail_valid == G::kUnitTok)  // only with nr.on: the new token closes its unit,
         fold_unit<T, D, BS, false>(st, q, kr, vr, scale_log2, row, active, G::kUnitTok);  // folded whole as without it
@@ -401,6 +393,34 @@ __device__ __forceinline__ void fold_prefix_states(const DecodeParams& prm, int 
   }
 }
 
+// pa_decode_append: the extra workgroup of sequence `seq` (grid row y = num_heads)
+// writes the sequence's new K and V row, every head, into the slot of its position
+// context_lens[seq] - 1.  The decode workgroups fold that row from new_key /
+// new_value, not from the pools: whatever they read in that slot while this
+// workgroup writes it is replaced in registers, so the two never wait on each other.
+// The pools are written only by pa_decode_append, whose caller passes them writable.
+template <typename T, int D, int BS, int kThreads>
+__device__ __forceinline__ void store_new_row(const DecodeParams& prm, int seq) {
+  const int ctx = prm.context_lens[seq];
+  if (ctx <= 0) return;
+  const int pos = ctx - 1;
+  const int blk = prm.block_tables[static_cast<size_t>(seq) * prm.max_blocks_per_seq + pos / BS];
+  constexpr int kChunks = D * static_cast<int>(sizeof(T)) / 16;  // 16-byte chunks per row
+  constexpr int kElems = 16 / static_cast<int>(sizeof(T));
+  const size_t src_row = static_cast<size_t>(seq) * prm.num_heads;
+  const size_t dst_row = static_cast<size_t>(blk) * prm.num_heads;
+  T* k_pool = static_cast<T*>(const_cast<void*>(prm.key_cache));
+  T* v_pool = static_cast<T*>(const_cast<void*>(prm.value_cache));
+  for (int t = threadIdx.x; t < prm.num_heads * kChunks; t += kThreads) {
+    const int h = t / kChunks;
+    const int c = t - h * kChunks;
+    const size_t src = (src_row + h) * D + static_cast<size_t>(c) * kElems;
+    const size_t dst = ((dst_row + h) * BS + pos % BS) * D + static_cast<size_t>(c) * kElems;
+    store16(k_pool + dst, load16(static_cast<const T*>(prm.new_key) + src));
+    store16(v_pool + dst, load16(static_cast<const T*>(prm.new_value) + src));
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // decode, partition pass
 // grid (max partitions, heads, seqs), W wave64s
@@ -415,6 +435,10 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
   const int part = blockIdx.x;
   const int head = blockIdx.y;
   const int seq = blockIdx.z;
+  if (head == prm.num_heads) {  // launched by pa_decode_append only
+    if (part == 0) store_new_row<T, D, BS, kThreads>(prm, seq);
+    return;
+  }
   const int P = prm.partition_tokens;
   const int start = prm.token_begin ? prm.token_begin[seq] : 0;  // a multiple of BS
   const int tok_begin = start + part * P;
@@ -467,9 +491,6 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
   const T* v_head = static_cast<const T*>(prm.value_cache) + static_cast<size_t>(head) * BS * D;
   const int lane_off = row * D + col_data * kVec;  // element offset of this lane in load 0
   const float scale_log2 = prm.scale * kLog2e;
-  // the pools are written only by pa_decode_append, whose caller passes them writable
-  nr.k_head = const_cast<T*>(k_head);
-  nr.v_head = const_cast<T*>(v_head);
 
   // This wave owns units first_unit + j * W, j < n_mine; the last of them may be
   // partly filled.
@@ -538,10 +559,6 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
         prm.ws_l[slot] = l;
       }
     }
-  }
-  if (nr.store) {  // pa_decode_append: the new row into the pools, waited on by no one
-    store16(nr.k_head + nr.at, nr.nk);
-    store16(nr.v_head + nr.at, nr.nv);
   }
 }
 
@@ -895,7 +912,8 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
 
 template <typename T, int D, int BS>
 static hipError_t launch_partitions_t(const DecodeParams& prm, hipStream_t stream) {
-  dim3 grid(prm.num_partitions, prm.num_heads, prm.num_seqs);
+  // pa_decode_append adds one row of workgroups (y = num_heads) that store the new rows
+  dim3 grid(prm.num_partitions, prm.num_heads + (prm.new_key ? 1 : 0), prm.num_seqs);
   if (prm.wide) {
     hipLaunchKernelGGL((decode_partitions_kernel<T, D, BS, kWavesWide>), grid, dim3(kWave * kWavesWide), 0,
                        stream, prm);

@@ -128,6 +128,7 @@ def _bad_decode_append(ops, **over):
     (dict(nv=None), 1),
     (dict(nk=(1 << 20) + 8), 2),   # misaligned new rows
     (dict(maxctx=64, P=16), 4),
+    (dict(H=65535), 2),            # the new rows take one more grid row of workgroups
 ])
 def test_decode_append_rejects_bad_arguments(ops, over, status):
     assert _bad_decode_append(ops, **over) == status

@@ -469,14 +469,15 @@ pa_status pa_decode_append(void* out, const void* query, void* key_cache, void* 
                              num_seqs, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                              max_context_len, scale, dtype, partition_size, workspace, workspace_bytes);
   if (st != PA_OK) return st;
-  if (num_heads >= kMaxGridYZ)  // one more grid row of workgroups stores the new rows
-    return fail(PA_ERR_INVALID_ARG, "num_heads %d must be < %d for pa_decode_append", num_heads, kMaxGridYZ);
   if (num_seqs == 0) return ok();
   if (!new_key || !new_value) return fail(PA_ERR_NULL, "new_key and new_value must not be NULL");
   if (!aligned16(new_key) || !aligned16(new_value))
     return fail(PA_ERR_INVALID_ARG, "new_key and new_value must be 16-byte aligned");
   plan.prm.new_key = new_key;
   plan.prm.new_value = new_value;
+  if (static_cast<int64_t>(num_seqs) + pa::store_slices(plan.prm) > kMaxGridYZ)  // store workgroups
+    return fail(PA_ERR_INVALID_ARG, "num_seqs %d leaves no room for the store workgroups (grid z <= %d)",
+                num_seqs, kMaxGridYZ);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   st = from_hip(pa::launch_decode_partitions(plan.prm, dtype == PA_F16, head_dim, block_size, hs),
                 "decode partition pass launch");

@@ -393,8 +393,9 @@ __device__ __forceinline__ void fold_prefix_states(const DecodeParams& prm, int 
   }
 }
 
-// pa_decode_append: the extra workgroup of sequence `seq` (grid row y = num_heads)
-// writes the sequence's new K and V row, every head, into the slot of its position
+// pa_decode_append: the store workgroup of sequence `seq` (one of the grid's extra
+// z-slices, dispatched after every decode workgroup, so they run in the launch's
+// tail) writes the sequence's new K and V row, every head, into the slot of its position
 // context_lens[seq] - 1.  The decode workgroups fold that row from new_key /
 // new_value, not from the pools: whatever they read in that slot while this
 // workgroup writes it is replaced in registers, so the two never wait on each other.
@@ -435,8 +436,10 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
   const int part = blockIdx.x;
   const int head = blockIdx.y;
   const int seq = blockIdx.z;
-  if (head == prm.num_heads) {  // launched by pa_decode_append only
-    if (part == 0) store_new_row<T, D, BS, kThreads>(prm, seq);
+  if (seq >= prm.num_seqs) {  // pa_decode_append's store workgroups, one per sequence
+    const int64_t s = (static_cast<int64_t>(seq - prm.num_seqs) * prm.num_heads + head) *
+                          prm.num_partitions + part;
+    if (s < prm.num_seqs) store_new_row<T, D, BS, kThreads>(prm, static_cast<int>(s));
     return;
   }
   const int P = prm.partition_tokens;
@@ -910,10 +913,19 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
 // launchers
 // ---------------------------------------------------------------------------------
 
+// z-slices of store workgroups pa_decode_append adds: one workgroup per sequence,
+// num_partitions * num_heads of them per slice
+int32_t store_slices(const DecodeParams& prm) {
+  if (!prm.new_key || prm.num_seqs == 0) return 0;
+  const int64_t per_slice = static_cast<int64_t>(prm.num_partitions) * prm.num_heads;
+  return static_cast<int32_t>((prm.num_seqs + per_slice - 1) / per_slice);
+}
+
 template <typename T, int D, int BS>
 static hipError_t launch_partitions_t(const DecodeParams& prm, hipStream_t stream) {
-  // pa_decode_append adds one row of workgroups (y = num_heads) that store the new rows
-  dim3 grid(prm.num_partitions, prm.num_heads + (prm.new_key ? 1 : 0), prm.num_seqs);
+  // pa_decode_append adds z-slices after the last sequence: one workgroup per sequence
+  // stores its new rows
+  dim3 grid(prm.num_partitions, prm.num_heads, prm.num_seqs + store_slices(prm));
   if (prm.wide) {
     hipLaunchKernelGGL((decode_partitions_kernel<T, D, BS, kWavesWide>), grid, dim3(kWave * kWavesWide), 0,
                        stream, prm);

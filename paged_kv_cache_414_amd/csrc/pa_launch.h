@@ -109,6 +109,8 @@ struct CopyParams {
   int64_t block_bytes;  // heads * block_size * head_dim * element size
 };
 
+// z-slices of store workgroups the partition pass adds for pa_decode_append (0 otherwise)
+int32_t store_slices(const DecodeParams& prm);
 hipError_t launch_decode_partitions(const DecodeParams& prm, bool f16, int head_dim,
                                     int block_size, hipStream_t stream);
 hipError_t launch_decode_reduce(const ReduceParams& prm, bool f16, int head_dim,

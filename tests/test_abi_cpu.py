@@ -128,7 +128,7 @@ def _bad_decode_append(ops, **over):
     (dict(nv=None), 1),
     (dict(nk=(1 << 20) + 8), 2),   # misaligned new rows
     (dict(maxctx=64, P=16), 4),
-    (dict(H=65535), 2),            # the new rows take one more grid row of workgroups
+    (dict(S=65535, H=1, MB=4), 2),  # the store workgroups take grid z-slices after the sequences
 ])
 def test_decode_append_rejects_bad_arguments(ops, over, status):
     assert _bad_decode_append(ops, **over) == status

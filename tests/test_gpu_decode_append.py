@@ -115,6 +115,8 @@ CASES = [
     (np.float32, 128, 16, 10, 3, (1, 500), 64),
     # 16-wave workgroups (at least 1024 workgroups of 32 units or more)
     (np.float16, 128, 16, 32, 32, (1, 1200), 0),
+    # one head, one partition: the store workgroups take 300 z-slices after the sequences
+    (np.float16, 64, 16, 300, 1, (1, 100), 0),
 ]
 
 

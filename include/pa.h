@@ -184,10 +184,11 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
  * attention takes the new row from new_key / new_value; one extra workgroup per
  * sequence stores it into the pools while the attention runs, so the slot must be
  * read by no other sequence of the call (copy-on-write carried out before, as
- * pa_cache_append requires distinct slots).  num_heads must be below 65535 (the extra
- * workgroups take one more grid row).  Other arguments, workspace and errors as
- * pa_decode; the same workspace size.  Saves the separate append launch, which is
- * most of a step's time at small batch.
+ * pa_cache_append requires distinct slots).  The store workgroups take
+ * ceil(num_seqs / (partitions x num_heads)) grid z-slices after the sequences', and
+ * num_seqs plus those must not exceed 65535 (PA_ERR_INVALID_ARG otherwise).  Other
+ * arguments, workspace and errors as pa_decode; the same workspace size.  Saves the
+ * separate append launch, which is most of a step's time at small batch.
  */
 pa_status pa_decode_append(void* out, const void* query, void* key_cache, void* value_cache,
                            const void* new_key, const void* new_value,

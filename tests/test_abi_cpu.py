@@ -129,6 +129,7 @@ def _bad_decode_append(ops, **over):
     (dict(nk=(1 << 20) + 8), 2),   # misaligned new rows
     (dict(maxctx=64, P=16), 4),
     (dict(S=65535, H=1, MB=4), 2),  # the store workgroups take grid z-slices after the sequences
+    (dict(S=32768, H=1, MB=4), 2),  # 32,768 sequences + 32,768 store workgroups > 65,535
 ])
 def test_decode_append_rejects_bad_arguments(ops, over, status):
     assert _bad_decode_append(ops, **over) == status

@@ -145,3 +145,15 @@ def test_decode_append_on_the_llama_shaped_batch():
     new_k = workloads.normal(rng, b.q.shape, b.dtype)
     new_v = workloads.normal(rng, b.q.shape, b.dtype)
     _run(b, b.context_lens.copy(), new_k, new_v, 0, check_oracle_rows=[0, 17, 41, 95])
+
+
+def test_decode_append_with_the_most_sequences_one_launch_takes():
+    """One head, one partition: 32,767 sequences and as many store workgroups fill the
+    grid's z range to 65,534 (one more sequence is refused on the host)."""
+    b = workloads.make_static_batch("append_max", seed=47, num_seqs=32767, num_heads=1, head_dim=64,
+                                    block_size=16, ctx_low=0, ctx_high=3, dtype=np.float16,
+                                    pool_slack=1.1)
+    rng = np.random.default_rng(47)
+    new_k = workloads.normal(rng, b.q.shape, np.float16)
+    new_v = workloads.normal(rng, b.q.shape, np.float16)
+    _run(b, b.context_lens.copy(), new_k, new_v, 0)

@@ -37,8 +37,9 @@ METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
 # known-size block copy (FETCH_SIZE x 1.9987, WRITE_SIZE x 1.000); the commands and
 # raw values are in profiles/decode_partitions_llama7b_pmc.md.  Valid only for the
-# kernel sources they were taken on (sha256 of the kernel file followed by the
-# launch header, whose constants the kernels use).
+# kernel sources and launch policy they were taken on (sha256 of the kernel file, the
+# launch header whose constants the kernels use, and the host code that picks the
+# partition length and the workgroup size of a launch).
 MEASURED_TRAFFIC = {
     "kernel_source_sha256": "f7c420fd492260d8b70bc36c081eade59315f289885b29b478e2296e98044607",
     "seed": 2,
@@ -48,7 +49,7 @@ MEASURED_TRAFFIC = {
 }
 KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                "paged_kv_cache_414_amd", "csrc", name)
-                  for name in ("pa_kernels.hip", "pa_launch.h")]
+                  for name in ("pa_kernels.hip", "pa_launch.h", "pa_api.cpp")]
 
 
 def kernel_sources_sha256() -> str:
@@ -78,8 +79,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition, 0 = auto")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="time budget of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of each leg of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--no-mixes", dest="mixes", action="store_false",
                     help="skip the continuous-batching and shared-prefix step mixes")
     ap.add_argument("--no-extras", dest="extras", action="store_false",
@@ -132,42 +133,120 @@ def launch_spread(fn, n, torch):
             "p90_ms": round(float(p90), 5)}
 
 
-def cpu_baseline(batch, budget_s):
-    """The oracle as it stands, single-threaded BLAS, over the batch's (seq, head)
-    pairs in order, repeating the batch until the time budget is spent."""
+# Worker processes the multi-core leg of the CPU baseline may use: the CPU share of a
+# one-GPU machine, whatever more the affinity mask shows.
+CPU_POOL_LIMIT = 16
+
+
+def _oracle_pairs(batch, budget_s, worker, workers, start):
+    """(pairs, tokens) the oracle finished between `start` and `start + budget_s`
+    (time.time() clock), taking the batch's (seq, head) pairs worker, worker +
+    workers, ... in order and repeating the batch."""
     import oracle
+
+    h_count = batch.num_heads
+    n_pairs = batch.num_seqs * h_count
+    pairs = tokens = 0
+    i = worker
+    while time.time() < start + budget_s:
+        s, h = divmod(i % n_pairs, h_count)
+        oracle.decode_one(batch.q[s, h], batch.k_pool, batch.v_pool, batch.block_tables[s],
+                          batch.context_lens[s], h, batch.scale)
+        tokens += int(batch.context_lens[s])
+        pairs += 1
+        i += workers
+    return pairs, tokens
+
+
+class _MappedBatch:
+    """The arrays of a decode batch the oracle reads, memory-mapped read-only from the
+    files a parent process wrote (no copy per worker)."""
+
+    def __init__(self, folder, meta):
+        for name in ("q", "k_pool", "v_pool", "block_tables", "context_lens"):
+            setattr(self, name, np.load(os.path.join(folder, name + ".npy"), mmap_mode="r"))
+        self.num_seqs, self.num_heads, self.scale = meta
+
+
+def _pool_worker(folder, meta, budget_s, worker, workers, start):
+    """One worker process of the multi-core leg (a fresh interpreter)."""
     from threadpoolctl import threadpool_limits
+
+    batch = _MappedBatch(folder, meta)
+    with threadpool_limits(limits=1):
+        while time.time() < start:
+            time.sleep(0.01)
+        return _oracle_pairs(batch, budget_s, worker, workers, start)
+
+
+def _multi_core_leg(batch, budget_s, workers):
+    """The oracle over the batch's pairs in `workers` fresh worker processes (spawned,
+    so none of them inherits this process's GPU state), all starting at one wall-clock
+    time and stopping `budget_s` seconds later; (pairs, tokens) summed."""
+    import multiprocessing
+    import shutil
+    import tempfile
+    from concurrent.futures import ProcessPoolExecutor
+
+    folder = tempfile.mkdtemp(prefix="pa_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        for name in ("q", "k_pool", "v_pool", "block_tables", "context_lens"):
+            np.save(os.path.join(folder, name + ".npy"), np.ascontiguousarray(getattr(batch, name)))
+        meta = (batch.num_seqs, batch.num_heads, batch.scale)
+        ctx = multiprocessing.get_context("spawn")
+        with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as pool:
+            start = time.time() + 5.0  # time for every worker to start and map the files
+            futs = [pool.submit(_pool_worker, folder, meta, budget_s, w, workers, start)
+                    for w in range(workers)]
+            done = [f.result() for f in futs]
+    finally:
+        shutil.rmtree(folder, ignore_errors=True)
+    return sum(p for p, _ in done), sum(t for _, t in done)
+
+
+def cpu_baseline(batch, budget_s):
+    """The oracle as it stands on the host's cores, two legs of `budget_s` seconds
+    each over the batch's (seq, head) pairs, BLAS limited to one thread per call: one
+    thread in this process, then one worker process per available core (at most
+    CPU_POOL_LIMIT).  Under a profiler that preloads itself into every process, the
+    multi-core leg is skipped (its workers would each open the GPU)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from paged_kv_cache_414_amd import metrics
 
+    cores_available = len(os.sched_getaffinity(0))
+    blas_default = max([int(i.get("num_threads", 1)) for i in threadpool_info()
+                        if i.get("user_api") == "blas"] or [1])
+    per_token = metrics.kv_bytes_per_token(1, 1, batch.head_dim, batch.q.itemsize)
     h_count = batch.num_heads
-    done_tokens = 0
-    pairs = 0
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            for s in range(batch.num_seqs):
-                for h in range(h_count):
-                    oracle.decode_one(batch.q[s, h], batch.k_pool, batch.v_pool,
-                                      batch.block_tables[s], batch.context_lens[s], h,
-                                      batch.scale)
-                    done_tokens += int(batch.context_lens[s])
-                    pairs += 1
-                    if time.perf_counter() - t0 >= budget_s:
-                        break
-                else:
-                    continue
-                break
-        elapsed = time.perf_counter() - t0
-    nbytes = metrics.kv_bytes_per_token(1, 1, batch.head_dim, batch.q.itemsize) * done_tokens
+        t0 = time.time()
+        pairs1, tokens1 = _oracle_pairs(batch, budget_s, 0, 1, t0)
+        el1 = time.time() - t0
+    gbps1 = metrics.gbps(per_token * tokens1, el1)
+    single = {"value": round(gbps1, 4), "unit": "GB/s", "cores": 1,
+              "seq_steps_per_s": round(pairs1 / h_count / el1, 4)}
+    workers = max(1, min(cores_available, CPU_POOL_LIMIT))
+    profiled = "rocprof" in os.environ.get("LD_PRELOAD", "")
+    if workers > 1 and not profiled:
+        pairsn, tokensn = _multi_core_leg(batch, budget_s, workers)
+        gbpsn = metrics.gbps(per_token * tokensn, budget_s)
+        multi = (f"{workers} worker processes {pairsn} pairs ({tokensn} tokens, {budget_s:.1f} s); ")
+    else:
+        workers, pairsn, tokensn, gbpsn, multi = 1, pairs1, tokens1, gbps1, ""
     return {
-        "value": round(metrics.gbps(nbytes, elapsed), 4),
+        "value": round(gbpsn, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": workers,
+        "cores_available": cores_available,
+        "cores_used": workers,
+        "blas_threads_default": blas_default,
+        "blas_threads_per_call": 1,
         "kind": "oracle",
-        "sample": (f"{pairs} (seq, head) pairs of the batch in order, repeating the batch "
-                   f"({done_tokens} tokens, {elapsed:.1f} s), fp64 numpy, BLAS limited to 1 thread"),
-        "seq_steps_per_s": round(pairs / h_count / elapsed, 4),
+        "sample": (f"the batch's (seq, head) pairs in order, repeating the batch, fp64 numpy: "
+                   f"{multi}1 thread {pairs1} pairs ({tokens1} tokens, {el1:.1f} s)"),
+        "seq_steps_per_s": round(pairsn / h_count / (budget_s if workers > 1 else el1), 4),
+        "single_thread": single,
     }
 
 
@@ -635,8 +714,9 @@ def main():
     kv = metrics.decode_kv_bytes(ctx, h_count, d, batch.q.itemsize)
     value = metrics.gbps(kv, ms_step * 1e-3)
     waves = ops.pa_decode_waves(s_count, h_count, d, bs, max_ctx, args.partition)
-    # the step's launch moves the live K/V rows and the 96 appended rows (read + written)
-    launch_bytes = kv + metrics.append_bytes(s_count, h_count, d, batch.q.itemsize)
+    # the step's launch reads every live K/V row once (the 96 new rows from new_key /
+    # new_value, counted in kv since the contexts count them) and writes the 96 new rows
+    launch_bytes = kv + metrics.fused_append_bytes(s_count, h_count, d, batch.q.itemsize)
     achieved = metrics.gbps(launch_bytes, ms_step * 1e-3)
     achieved_alone = metrics.gbps(kv, ms_part * 1e-3)
     record = {
@@ -705,7 +785,7 @@ def main():
     if args.copy_probe:
         record["copy_probe"] = copy_probe(torch, ops, metrics)
     if args.cpu_seconds > 0:
-        log(args, f"CPU oracle baseline ({args.cpu_seconds:.0f} s budget)")
+        log(args, f"CPU oracle baseline ({args.cpu_seconds:.0f} s per leg)")
         record["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
     else:
         record["cpu_baseline"] = None

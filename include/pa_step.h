@@ -96,8 +96,9 @@ typedef struct pa_step_args {
   const int64_t* finished_ids;
   int32_t num_finished;
   /* Waiting requests (host): ids that are distinct and not known to the manager at
-   * the call, and their prompt lengths (>= 0, sum <= max_admit_tokens).  They are
-   * admitted in order while their blocks fit. */
+   * the call, and their prompt lengths (>= 0, each < max_blocks_per_seq * block_size
+   * so that the next decode token still fits the table row, sum <=
+   * max_admit_tokens).  They are admitted in order while their blocks fit. */
   const int64_t* admit_ids;
   const int32_t* admit_lens;
   int32_t num_admit;

@@ -11,7 +11,6 @@ from .paged_attention import (  # noqa: F401
     cache_append,
     decode,
     decode_one,
-    decode_pairs,
     gather_head,
     gather_head_fast,
     merge_partition_states,
@@ -19,6 +18,5 @@ from .paged_attention import (  # noqa: F401
     slot_of,
     slots_for_positions,
     swap_blocks,
-    to_float64,
     token_location,
 )

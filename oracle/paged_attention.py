@@ -129,15 +129,6 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale,
     return out
 
 
-def decode_pairs(q, k_pool, v_pool, block_tables, context_lens, scale, pairs):
-    """Outputs of selected (sequence, head) pairs only: float64 [len(pairs), D]."""
-    out = np.zeros((len(pairs), q.shape[2]), dtype=np.float64)
-    for i, (s, h) in enumerate(pairs):
-        out[i] = decode_one(q[s, h], k_pool, v_pool, block_tables[s], context_lens[s],
-                            h, scale)
-    return out
-
-
 # ----------------------------------------------------------------------------------
 # split-context partition states and their merge
 # ----------------------------------------------------------------------------------
@@ -275,8 +266,3 @@ def slots_for_positions(block_tables, seq_ids, positions, block_size):
     """Slot of (sequence, position) pairs, recomputed from the tables alone."""
     return np.array([slot_of(block_tables[s], p, block_size)
                      for s, p in zip(seq_ids, positions)], dtype=np.int64)
-
-
-def to_float64(x: np.ndarray) -> np.ndarray:
-    """Exact upcast of stored float16/float32 values."""
-    return np.asarray(x).astype(np.float64)

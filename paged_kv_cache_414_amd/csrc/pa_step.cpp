@@ -205,6 +205,12 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
   int64_t requested = 0;
   for (int32_t i = 0; i < a->num_admit; ++i) {
     if (a->admit_lens[i] < 0) return pa::set_error(PA_ERR_INVALID_ARG, "admit_lens[%d] is negative", i);
+    // an admitted prompt must leave room in its table row for the next decode token,
+    // or every later step that lists it would be refused
+    if (static_cast<int64_t>(a->admit_lens[i]) >= static_cast<int64_t>(mb) * bs)
+      return pa::set_error(PA_ERR_INVALID_ARG,
+                           "admit_lens[%d] = %d leaves no room for a decode token in %d blocks of %d tokens", i,
+                           a->admit_lens[i], mb, bs);
     if (pa_bm_num_seq_blocks(e->bm, a->admit_ids[i]) >= 0)
       return pa::set_error(PA_ERR_INVALID_ARG, "request id %lld is a known sequence", (long long)a->admit_ids[i]);
     requested += a->admit_lens[i];

@@ -45,6 +45,13 @@ def append_bytes(num_tokens: int, heads: int, head_dim: int, elem_bytes: int) ->
     return 2 * 2 * int(num_tokens) * int(heads) * int(head_dim) * int(elem_bytes)
 
 
+def fused_append_bytes(num_tokens: int, heads: int, head_dim: int, elem_bytes: int) -> int:
+    """What appending inside the decode launch adds to the decode's bytes: the new K
+    and V rows written.  Their read is already among the decode's live rows, since the
+    contexts count the new tokens."""
+    return 2 * int(num_tokens) * int(heads) * int(head_dim) * int(elem_bytes)
+
+
 def block_copy_bytes(num_pairs: int, heads: int, block_size: int, head_dim: int,
                      elem_bytes: int) -> int:
     """Read and write of K and V of every copied block."""

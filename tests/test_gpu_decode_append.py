@@ -39,7 +39,7 @@ def _nan_rows(pool, slots, bs):
         view[slot // bs, :, slot % bs, :] = bits
 
 
-def _run(b, ctx, new_k, new_v, part, check_oracle_rows=None):
+def _run(b, ctx, new_k, new_v, part):
     """The three ways; returns nothing, asserts everything."""
     from paged_kv_cache_414_amd import ops
     bs = b.block_size
@@ -80,10 +80,9 @@ def _run(b, ctx, new_k, new_v, part, check_oracle_rows=None):
         assert np.array_equal(got.cpu().numpy().view(itype), want.view(itype))
     o1, o2 = out1.cpu().numpy(), out2.cpu().numpy()
     assert np.array_equal(o2.view(itype), o1.view(itype)), "fused and two-call outputs differ"
-    rows = np.arange(len(ctx)) if check_oracle_rows is None else np.asarray(check_oracle_rows)
-    want = oracle.decode(b.q[rows], k_want, v_want, b.block_tables[rows], ctx[rows], b.scale)
-    assert np.all(np.isfinite(o2[rows]))
-    err = max_abs_err(o2[rows], want)
+    want = oracle.decode(b.q, k_want, v_want, b.block_tables, ctx, b.scale)
+    assert np.all(np.isfinite(o2))
+    err = max_abs_err(o2, want)
     assert err <= tol_for(b.dtype), err
 
 
@@ -138,13 +137,31 @@ def test_decode_append_matches_two_calls_and_oracle(case):
 
 def test_decode_append_on_the_llama_shaped_batch():
     """The benchmark's batch and launch (96 x 32 x 128, bs 16, library partition
-    choice): pools and every output bit for bit against the two-call step; a sample
-    of sequences against the oracle."""
+    choice, the new rows drawn as the benchmark draws them): pools bit for bit against
+    the oracle's append, and every one of the 96 x 32 outputs against the oracle's
+    decode over the appended pools, and bit for bit against the two-call step."""
     b = workloads.llama7b_decode(seed=2, poison=True)
     rng = np.random.default_rng([2, 7])
     new_k = workloads.normal(rng, b.q.shape, b.dtype)
     new_v = workloads.normal(rng, b.q.shape, b.dtype)
-    _run(b, b.context_lens.copy(), new_k, new_v, 0, check_oracle_rows=[0, 17, 41, 95])
+    _run(b, b.context_lens.copy(), new_k, new_v, 0)
+
+
+def test_decode_append_on_the_long_context_batch():
+    """The long-context batch (8 x 32 x 128, bs 32, contexts U[16384, 32768], 10,000
+    blocks) with the library's partition choice: two partitions per sequence, so each
+    new row falls in the second partition and the merge pass runs after the fused
+    launch.  Pools bit for bit, every output against the oracle."""
+    from paged_kv_cache_414_amd import ops
+    b = workloads.long_context(seed=5, poison=True)
+    assert ops.pa_decode_num_partitions(b.num_seqs, b.num_heads, b.block_size,
+                                        b.max_context_len) == 2
+    p = ops.pa_decode_partition_size(b.num_seqs, b.num_heads, b.block_size, b.max_context_len)
+    assert np.all(b.context_lens - 1 >= p)  # the new row sits in partition 1
+    rng = np.random.default_rng([5, 7])
+    new_k = workloads.normal(rng, b.q.shape, b.dtype)
+    new_v = workloads.normal(rng, b.q.shape, b.dtype)
+    _run(b, b.context_lens.copy(), new_k, new_v, 0)
 
 
 def test_decode_append_with_the_most_sequences_one_launch_takes():

@@ -147,6 +147,8 @@ def test_errors_leave_everything_unchanged():
                 "prompt_key": q, "prompt_value": q},  # request id already known
                {"ids": [0], "admit_ids": np.array([5]), "admit_lens": np.array([600]),
                 "prompt_key": big, "prompt_value": big},  # more prompt tokens than staged
+               {"ids": [0], "admit_ids": np.array([5, 6]), "admit_lens": np.array([3, 80]),
+                "prompt_key": big, "prompt_value": big},  # fills all 5 blocks: no room left
                {"ids": [0], "group_starts": np.array([0, 1], dtype=np.int32)}):  # no groups
         ids = kw.pop("ids")
         with pytest.raises(ops.PagedAttentionError):

@@ -27,3 +27,10 @@ def test_decode_bytes_count_live_tokens_only():
     ctx = np.array([1, 17, 300])
     assert metrics.decode_kv_bytes(ctx, 32, 128, 2) == 318 * 16384
     assert metrics.decode_flops(ctx, 32, 128) == 4 * 318 * 32 * 128
+
+
+def test_fused_append_adds_only_the_written_rows():
+    # 96 new tokens of 32 heads x 128 fp16: written once, K and V (their read is among
+    # the live rows the decode bytes already count)
+    assert metrics.fused_append_bytes(96, 32, 128, 2) == 96 * 16384
+    assert metrics.append_bytes(96, 32, 128, 2) == 2 * metrics.fused_append_bytes(96, 32, 128, 2)

@@ -151,6 +151,22 @@ def test_slot_of_block_table_example():
     assert oracle.token_location(t2, 16, 16) == (9, 0)
 
 
+def test_slots_for_positions_block_table_example():
+    """The batch form the step replays use, on the same sketch stacked into one
+    [2, 3] table (seq_2's unused third entry padded with a value no slot may come
+    from): (seq_1, 0) -> 48, (seq_1, 17) -> 113, (seq_1, 39) -> 199, (seq_2, 31) ->
+    159, (seq_2, 16) -> block 9 offset 0 = 144, (seq_2, 0) -> block 5 offset 0 = 80."""
+    ex = pins.load_block_table_example()
+    t1, t2 = ex["tables"]["seq_1"], ex["tables"]["seq_2"]
+    tables = np.array([t1, t2 + [-1000]], dtype=np.int32)
+    got = oracle.slots_for_positions(tables, [0, 0, 0, 1, 1, 1], [0, 17, 39, 31, 16, 0],
+                                     ex["block_size"])
+    assert got.tolist() == [48, 113, 199, 159, 144, 80]
+    # the sequence index selects the row: the same positions on the other row differ
+    swapped = oracle.slots_for_positions(tables, [1, 1], [0, 17], ex["block_size"])
+    assert swapped.tolist() == [80, 145]
+
+
 def _append_case():
     rng = np.random.default_rng(0)
     k = rng.standard_normal((16, 2, 16, 4)).astype(np.float16)

@@ -200,6 +200,50 @@ pa_status pa_decode_append(void* out, const void* query, void* key_cache, void* 
                            void* stream);
 
 /*
+ * Launch hints for pa_decode_ex and pa_decode_append_ex: what a caller that knows its
+ * batch (a scheduler holds every context length on the host) can tell the library.
+ * Pools are written bit for bit as without hints, and outputs stay within the stated
+ * tolerance of the exact attention.
+ *   seq_order  device int32 [num_seqs], 4-byte aligned, or NULL: a permutation of
+ *              0 .. num_seqs-1 (caller precondition, unchecked device data); the
+ *              workgroups of sequence seq_order[i] are dispatched i-th.  Longest
+ *              context first lets the short sequences fill the end of the launch.
+ *              The order changes no bit of the result: every floating-point
+ *              operation's order depends only on logical token positions.
+ *   waves      wave64s per workgroup of the partition pass: 0 for the library's
+ *              choice (pa_decode_waves), else 8 or 16 (PA_ERR_INVALID_ARG otherwise).
+ *              The wave count sets how a partition's tokens are dealt to waves and
+ *              merged, so it changes the rounding of the output (bit for bit that of
+ *              any call launched with the same count).  8 suits batches whose
+ *              sequences re-read shared blocks through pa_decode (the caches serve
+ *              the re-reads better with more, smaller workgroups in flight).
+ */
+typedef struct pa_decode_hints {
+  const int32_t* seq_order;
+  int32_t waves;
+} pa_decode_hints;
+
+/* pa_decode with launch hints (NULL hints = pa_decode). */
+pa_status pa_decode_ex(void* out, const void* query, const void* key_cache,
+                       const void* value_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                       pa_dtype dtype, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, const pa_decode_hints* hints, void* stream);
+
+/* pa_decode_append with launch hints (NULL hints = pa_decode_append). */
+pa_status pa_decode_append_ex(void* out, const void* query, void* key_cache, void* value_cache,
+                              const void* new_key, const void* new_value,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                              pa_dtype dtype, int32_t partition_size, void* workspace,
+                              size_t workspace_bytes, const pa_decode_hints* hints,
+                              void* stream);
+
+/*
  * pa_decode_partitions -- first pass of pa_decode alone (same arguments).
  * Sequences with L <= P get their final output written to `out`; for the others,
  * every partition p < ceil(L / P) writes its (m, l, o) state to the workspace and

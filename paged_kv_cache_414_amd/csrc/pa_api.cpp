@@ -235,6 +235,19 @@ pa_status plan_decode(DecodePlan* plan, void* out, const void* query, const void
   return PA_OK;
 }
 
+// Caller hints on top of the library's plan: a dispatch order and a workgroup size.
+pa_status apply_hints(DecodePlan* plan, const pa_decode_hints* hints) {
+  if (!hints) return PA_OK;
+  if (hints->waves != 0 && hints->waves != pa::kDecodeWavesNarrow && hints->waves != pa::kDecodeWavesWide)
+    return fail(PA_ERR_INVALID_ARG, "hints->waves %d is not 0, %d or %d", hints->waves, pa::kDecodeWavesNarrow,
+                pa::kDecodeWavesWide);
+  if (hints->seq_order && (reinterpret_cast<uintptr_t>(hints->seq_order) & 3u) != 0)
+    return fail(PA_ERR_INVALID_ARG, "hints->seq_order must be 4-byte aligned");
+  if (hints->waves != 0) plan->prm.wide = hints->waves == pa::kDecodeWavesWide ? 1 : 0;
+  plan->prm.seq_order = hints->seq_order;
+  return PA_OK;
+}
+
 // Library choice of the prefix partition length (tokens of the shared prefix that
 // one workgroup reads for a tile of 16 of a group's queries): the whole longest
 // prefix, halved while fewer than kPrefixMinUnits (group, query tile, head,
@@ -388,6 +401,26 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
   return workspace_bytes_for(num_seqs, num_heads, head_dim, partitions_for(max_context_len, P));
 }
 
+static pa_status decode_partitions_hinted(void* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                          int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                          pa_dtype dtype, int32_t partition_size, void* workspace,
+                                          size_t workspace_bytes, const pa_decode_hints* hints, void* stream) {
+  DecodePlan plan;
+  pa_status st = plan_decode(&plan, out, query, key_cache, value_cache, block_tables, context_lens,
+                             num_seqs, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             max_context_len, scale, dtype, partition_size, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  st = apply_hints(&plan, hints);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  return from_hip(pa::launch_decode_partitions(plan.prm, dtype == PA_F16, head_dim, block_size,
+                                               static_cast<hipStream_t>(stream)),
+                  "decode partition pass launch");
+}
+
 pa_status pa_decode_partitions(void* out, const void* query, const void* key_cache,
                                const void* value_cache, const int32_t* block_tables,
                                const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
@@ -395,15 +428,10 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
                                int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                                pa_dtype dtype, int32_t partition_size, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  DecodePlan plan;
-  pa_status st = plan_decode(&plan, out, query, key_cache, value_cache, block_tables, context_lens,
-                             num_seqs, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                             max_context_len, scale, dtype, partition_size, workspace, workspace_bytes);
-  if (st != PA_OK) return st;
-  if (num_seqs == 0) return ok();
-  return from_hip(pa::launch_decode_partitions(plan.prm, dtype == PA_F16, head_dim, block_size,
-                                               static_cast<hipStream_t>(stream)),
-                  "decode partition pass launch");
+  return decode_partitions_hinted(out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                                  num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                  max_context_len, scale, dtype, partition_size, workspace, workspace_bytes,
+                                  nullptr, stream);
 }
 
 pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
@@ -444,30 +472,44 @@ pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_by
                   "decode reduce pass launch");
 }
 
-pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
-                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                    int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
-                    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
-  pa_status st = pa_decode_partitions(out, query, key_cache, value_cache, block_tables, context_lens,
-                                      num_seqs, num_heads, head_dim, block_size, num_blocks,
-                                      max_blocks_per_seq, max_context_len, scale, dtype, partition_size,
-                                      workspace, workspace_bytes, stream);
+pa_status pa_decode_ex(void* out, const void* query, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                       const pa_decode_hints* hints, void* stream) {
+  pa_status st = decode_partitions_hinted(out, query, key_cache, value_cache, block_tables, context_lens,
+                                          num_seqs, num_heads, head_dim, block_size, num_blocks,
+                                          max_blocks_per_seq, max_context_len, scale, dtype, partition_size,
+                                          workspace, workspace_bytes, hints, stream);
   if (st != PA_OK) return st;
   return pa_decode_reduce(out, workspace, workspace_bytes, context_lens, num_seqs, num_heads, head_dim,
                           block_size, max_context_len, dtype, partition_size, stream);
 }
 
-pa_status pa_decode_append(void* out, const void* query, void* key_cache, void* value_cache,
-                           const void* new_key, const void* new_value, const int32_t* block_tables,
-                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
-                           int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_decode_ex(out, query, key_cache, value_cache, block_tables, context_lens, num_seqs, num_heads,
+                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                      partition_size, workspace, workspace_bytes, nullptr, stream);
+}
+
+pa_status pa_decode_append_ex(void* out, const void* query, void* key_cache, void* value_cache,
+                              const void* new_key, const void* new_value, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+                              int32_t partition_size, void* workspace, size_t workspace_bytes,
+                              const pa_decode_hints* hints, void* stream) {
   DecodePlan plan;
   pa_status st = plan_decode(&plan, out, query, key_cache, value_cache, block_tables, context_lens,
                              num_seqs, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                              max_context_len, scale, dtype, partition_size, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  st = apply_hints(&plan, hints);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return ok();
   if (!new_key || !new_value) return fail(PA_ERR_NULL, "new_key and new_value must not be NULL");
@@ -484,6 +526,18 @@ pa_status pa_decode_append(void* out, const void* query, void* key_cache, void* 
   if (st != PA_OK) return st;
   return pa_decode_reduce(out, workspace, workspace_bytes, context_lens, num_seqs, num_heads, head_dim,
                           block_size, max_context_len, dtype, partition_size, stream);
+}
+
+pa_status pa_decode_append(void* out, const void* query, void* key_cache, void* value_cache,
+                           const void* new_key, const void* new_value, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_decode_append_ex(out, query, key_cache, value_cache, new_key, new_value, block_tables, context_lens,
+                             num_seqs, num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             max_context_len, scale, dtype, partition_size, workspace, workspace_bytes, nullptr,
+                             stream);
 }
 
 pa_status pa_cache_append(void* key_cache, void* value_cache, const void* key, const void* value,

@@ -435,13 +435,15 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
 
   const int part = blockIdx.x;
   const int head = blockIdx.y;
-  const int seq = blockIdx.z;
-  if (seq >= prm.num_seqs) {  // pa_decode_append's store workgroups, one per sequence
-    const int64_t s = (static_cast<int64_t>(seq - prm.num_seqs) * prm.num_heads + head) *
+  const int z = blockIdx.z;
+  if (z >= prm.num_seqs) {  // pa_decode_append's store workgroups, one per sequence
+    const int64_t s = (static_cast<int64_t>(z - prm.num_seqs) * prm.num_heads + head) *
                           prm.num_partitions + part;
     if (s < prm.num_seqs) store_new_row<T, D, BS, kThreads>(prm, static_cast<int>(s));
     return;
   }
+  // grid slice z decodes sequence z, or seq_order[z] when the caller ordered the launch
+  const int seq = prm.seq_order ? __builtin_amdgcn_readfirstlane(prm.seq_order[z]) : z;
   const int P = prm.partition_tokens;
   const int start = prm.token_begin ? prm.token_begin[seq] : 0;  // a multiple of BS
   const int tok_begin = start + part * P;

@@ -47,6 +47,9 @@ struct DecodeParams {
   // for a plain decode.  Only with token_begin == nullptr.
   const void* new_key = nullptr;
   const void* new_value = nullptr;
+  // [S] or nullptr: the workgroups of grid slice z decode sequence seq_order[z] (a
+  // permutation of the batch), so the caller chooses the dispatch order
+  const int32_t* seq_order = nullptr;
 };
 
 // Prefix pass of the shared-prefix decode: one workgroup per (prefix partition,

@@ -36,6 +36,10 @@ SIGNATURES = {
                          _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_decode_append": (_i32, [_vp] * 8 + [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                              _i32, _vp, _sz, _vp]),
+    "pa_decode_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                            _i32, _f32, _i32, _i32, _vp, _sz, _vp, _vp]),
+    "pa_decode_append_ex": (_i32, [_vp] * 8 + [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                                _i32, _i32, _vp, _sz, _vp, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -71,6 +75,22 @@ SIGNATURES = {
     "pa_step_run": (_i32, [_vp, _vp, _vp, _vp]),
     "pa_step_last": (_i32, [_vp, _vp]),
 }
+
+
+class DecodeHints(ctypes.Structure):
+    """pa_decode_hints of include/pa.h: a dispatch order and a workgroup size."""
+    _fields_ = [("seq_order", _vp), ("waves", _i32)]
+
+
+def _hints(seq_order, waves, device):
+    """A DecodeHints for the call, or None when neither hint is given."""
+    if seq_order is None and not waves:
+        return None
+    if seq_order is not None:
+        _int32(seq_order)
+        if seq_order.dim() != 1 or seq_order.get_device() != device:
+            raise ValueError("seq_order must be a 1-D int32 tensor on the call's GPU")
+    return ctypes.byref(DecodeHints(_ptr(seq_order) if seq_order is not None else None, int(waves)))
 
 
 class PagedAttentionError(RuntimeError):
@@ -217,27 +237,39 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
 
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
-              max_context_len, partition_size=0, workspace=None, stream=None):
-    """Paged decode attention into ``out`` [S, H, D] (see include/pa.h)."""
-    _check(lib.pa_decode(*_decode_args(out, query, key_cache, value_cache, block_tables,
-                                       context_lens, scale, max_context_len,
-                                       partition_size, workspace, stream)))
+              max_context_len, partition_size=0, workspace=None, stream=None, seq_order=None,
+              waves=0):
+    """Paged decode attention into ``out`` [S, H, D] (see include/pa.h).  With
+    ``seq_order`` (int32 [S] on the GPU, a permutation) or ``waves`` (8 or 16) the call
+    is pa_decode_ex with those launch hints."""
+    args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                        max_context_len, partition_size, workspace, stream)
+    hints = _hints(seq_order, waves, query.get_device())
+    if hints is None:
+        _check(lib.pa_decode(*args))
+    else:
+        _check(lib.pa_decode_ex(*args[:-1], hints, args[-1]))
     return out
 
 
 def pa_decode_append(out, query, key_cache, value_cache, new_key, new_value, block_tables,
                      context_lens, scale, max_context_len, partition_size=0, workspace=None,
-                     stream=None):
+                     stream=None, seq_order=None, waves=0):
     """Append each sequence's newest K/V row ``new_key`` / ``new_value`` [S, H, D] at
     position context_lens[s] - 1, then paged decode attention into ``out``, in one
-    call (see include/pa.h)."""
+    call (see include/pa.h); with launch hints as :func:`pa_decode`."""
     args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                         max_context_len, partition_size, workspace, stream)
     _same_device(query, new_key, new_value)
     for name, t in (("new_key", new_key), ("new_value", new_value)):
         if t.dtype != query.dtype or t.shape != query.shape or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {query.dtype} tensor shaped like query")
-    _check(lib.pa_decode_append(*args[:4], _ptr(new_key), _ptr(new_value), *args[4:]))
+    hints = _hints(seq_order, waves, query.get_device())
+    if hints is None:
+        _check(lib.pa_decode_append(*args[:4], _ptr(new_key), _ptr(new_value), *args[4:]))
+    else:
+        _check(lib.pa_decode_append_ex(*args[:4], _ptr(new_key), _ptr(new_value), *args[4:-1],
+                                       hints, args[-1]))
     return out
 
 

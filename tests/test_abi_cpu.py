@@ -275,3 +275,21 @@ def test_last_error_is_per_thread(ops):
     for t in threads:
         t.join()
     assert not bad, bad[:3]
+
+
+def test_decode_hints_are_checked_on_the_host(ops):
+    """pa_decode_ex / pa_decode_append_ex: a workgroup size other than 0, 8 or 16 and a
+    misaligned order are refused before launch; NULL hints behave as the plain call."""
+    fake = 1 << 20
+    lib = ops.lib
+    base = (fake, fake, fake, fake, fake, fake, 4, 4, 64, 16, 64, 4, 64, 0.125, ops.PA_F32, 0,
+            None, 0)
+    for waves, order, status in ((12, None, 2), (8, fake + 2, 2)):
+        h = ops.DecodeHints(order, waves)
+        assert lib.pa_decode_ex(*base, ctypes.byref(h), None) == status
+        assert b"hints" in lib.pa_last_error()
+        assert lib.pa_decode_append_ex(*base[:4], fake, fake, *base[4:], ctypes.byref(h),
+                                       None) == status
+    # NULL hints and an empty batch: nothing to do
+    empty = (None,) * 6 + (0,) + base[7:]
+    assert lib.pa_decode_ex(*empty, None, None) == 0

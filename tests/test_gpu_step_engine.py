@@ -91,7 +91,7 @@ def _pools_equal(kc, vc, host):
 
 
 def test_admission_stops_at_the_first_request_that_does_not_fit():
-    bm, kc, vc, eng, host = _setup(nb=24, seed=5)
+    bm, kc, vc, eng, host = _setup(nb=24, seed=5, mb=32)  # rows of 512 tokens: every prompt fits a row
     rng = np.random.default_rng(1)
     for sid, n in ((0, 40), (1, 17)):  # 3 + 2 blocks: 19 free
         _seed_sequence(bm, kc, vc, host, rng, sid, n)

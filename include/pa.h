@@ -244,6 +244,31 @@ pa_status pa_decode_append_ex(void* out, const void* query, void* key_cache, voi
                               void* stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device memory: code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, result and errors as pa_decode, without the workspace: when some
+ * sequence spans more than one partition, the partition states go to a scratch array
+ * that the library holds in device memory (a file-scope device variable of
+ * PA_NOALLOC_SCRATCH_BYTES bytes on every GPU the library runs on, kept until the
+ * process ends; the call allocates nothing).  Arguments whose
+ * pa_decode_workspace_bytes(...) exceeds that size return PA_ERR_WORKSPACE before
+ * anything is enqueued.  The first call that needs the array on a device looks up its
+ * address there (make it before capturing a graph).  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's partition states: calls that overlap on one
+ * GPU (different streams, or host threads not ordered by the caller) race and give
+ * undefined results; calls in one stream are ordered.  Nothing in the array needs to
+ * start at zero.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+pa_status pa_decode_noalloc(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                            pa_dtype dtype, int32_t partition_size, void* stream);
+
+/*
  * pa_decode_partitions -- first pass of pa_decode alone (same arguments).
  * Sequences with L <= P get their final output written to `out`; for the others,
  * every partition p < ceil(L / P) writes its (m, l, o) state to the workspace and

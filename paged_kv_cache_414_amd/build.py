@@ -20,7 +20,7 @@ INCLUDE = ROOT / "include"
 LIB = PKG / "libpa.so"
 BUILD_DIR = ROOT / "_build"
 
-SOURCES = [CSRC / "pa_kernels.hip", CSRC / "pa_copy.hip", CSRC / "pa_stage.hip",
+SOURCES = [CSRC / "pa_kernels.hip", CSRC / "pa_copy.hip", CSRC / "pa_stage.hip", CSRC / "pa_noalloc.hip",
            CSRC / "pa_api.cpp", CSRC / "pa_blocks.cpp", CSRC / "pa_step.cpp"]
 HEADERS = [INCLUDE / "pa.h", INCLUDE / "pa_blocks.h", INCLUDE / "pa_step.h", CSRC / "pa_launch.h", CSRC / "pa_status.h"]
 

@@ -18,6 +18,7 @@ LIB_PATH = pathlib.Path(__file__).resolve().with_name("libpa.so")
 
 PA_F32 = 0
 PA_F16 = 1
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20  # size of pa_decode_noalloc's scratch array (pa.h)
 _DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16}
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_INVALID_ARG", 3: "PA_ERR_UNSUPPORTED",
            4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP", 6: "PA_ERR_OUT_OF_BLOCKS"}
@@ -40,6 +41,8 @@ SIGNATURES = {
                             _i32, _f32, _i32, _i32, _vp, _sz, _vp, _vp]),
     "pa_decode_append_ex": (_i32, [_vp] * 8 + [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                                 _i32, _i32, _vp, _sz, _vp, _vp]),
+    "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _f32, _i32, _i32, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -249,6 +252,16 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
         _check(lib.pa_decode(*args))
     else:
         _check(lib.pa_decode_ex(*args[:-1], hints, args[-1]))
+    return out
+
+
+def pa_decode_noalloc(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                      max_context_len, partition_size=0, stream=None):
+    """pa_decode with the partition states in the library's own scratch array instead
+    of a caller workspace (see include/pa.h: for callers that cannot allocate)."""
+    args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                        max_context_len, partition_size, None, stream)
+    _check(lib.pa_decode_noalloc(*args[:16], args[18]))
     return out
 
 

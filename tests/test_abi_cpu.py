@@ -277,6 +277,27 @@ def test_last_error_is_per_thread(ops):
     assert not bad, bad[:3]
 
 
+def test_noalloc_scratch_size_and_host_checks(ops):
+    """pa_decode_noalloc: the binding's scratch size is the header's; invalid arguments
+    are refused by pa_decode's checks and oversize requests by the size check, both
+    before anything touches a GPU."""
+    text = (ROOT / "include" / "pa.h").read_text()
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ops.PA_NOALLOC_SCRATCH_BYTES
+    fake = 1 << 20
+    lib = ops.lib
+    assert lib.pa_decode_noalloc(fake, fake, fake, fake, fake, fake, 4, 4, 72, 16, 64, 4, 64,
+                                 0.125, ops.PA_F32, 0, None) == 3
+    assert lib.pa_decode_noalloc(fake, None, fake, fake, fake, fake, 4, 4, 64, 16, 64, 4, 64,
+                                 0.125, ops.PA_F32, 0, None) == 1
+    s, h, d, bs, mcl, part = 4096, 32, 128, 16, 8192, 512
+    assert lib.pa_decode_noalloc(fake, fake, fake, fake, fake, fake, s, h, d, bs, 100000,
+                                 mcl // bs, mcl, 0.1, ops.PA_F16, part, None) == 4
+    assert b"scratch" in lib.pa_last_error()
+    assert lib.pa_decode_noalloc(None, None, None, None, None, None, 0, 4, 64, 16, 64, 4, 64,
+                                 0.125, ops.PA_F32, 0, None) == 0
+
+
 def test_decode_hints_are_checked_on_the_host(ops):
     """pa_decode_ex / pa_decode_append_ex: a workgroup size other than 0, 8 or 16 and a
     misaligned order are refused before launch; NULL hints behave as the plain call."""

@@ -14,27 +14,32 @@
  *   2. block tables and context lengths (counting the new token) are built; when
  *      groups are given, a group's prefix is the run of leading whole blocks that
  *      all of its members hold;
- *   3. sequences that finished give their blocks back, and waiting requests are
- *      admitted in order while their blocks fit, stopping at the first that does
- *      not ([Reading vLLM] §3, the scheduler step; [vLLM basics] §2.4, continuous
- *      batching);
+ *   3. waiting requests are admitted in order while their blocks fit, stopping at
+ *      the first that does not ([Reading vLLM] §3, the scheduler step; [vLLM basics]
+ *      §2.4, continuous batching), then the sequences that finished give their blocks
+ *      back: a block given back in a step goes to new requests from the next step on,
+ *      so no prompt row of a step lands in a block that step's decode reads;
  *   4. every small array the device needs is written into a pinned host buffer of
  *      the executor and moved to the device by one small kernel that reads that
  *      buffer, on `stream` (so the kernels that follow wait on no DMA engine);
  *   5. on `stream`: pa_block_copy when copy-on-write pairs are due, pa_cache_append
- *      of the step's new K/V rows, the decode (pa_decode, or pa_decode_shared_prefix
- *      when groups are given), then pa_cache_append of the admitted prompts' rows.
- * A block given back in step 3 may go to an admitted request at once: its prompt
- * rows are written after the decode in stream order, so the decode still reads the
- * old contents.
+ *      of the step's new K/V rows (in the staging launch when no copy is due), then
+ *      the decode.  Without groups the decode is pa_decode_ex, whose launch also writes
+ *      the admitted prompts' rows in trailing workgroups, with 8-wave workgroups and,
+ *      unless some block of the batch is held by several sequences, the longest
+ *      contexts dispatched first; with groups it is pa_decode_shared_prefix followed by
+ *      pa_cache_append of the prompts' rows.
  *
  * Ownership.  Unlike the entry points of pa.h, an executor allocates: two pinned
- * host staging buffers and one device staging buffer (sized at creation) and a
- * device workspace for the decode (grown when a step needs more; before freeing the
- * old one the executor waits until its earlier steps have finished).  The block
+ * host staging buffers, a pinned host word into which each step's staging kernel
+ * writes its step number as it starts (the host reuses a staging buffer once the step
+ * after the one that read it has started: no event is recorded per step), one device
+ * staging buffer (sized at creation) and a device workspace for the decode (grown
+ * when a step needs more; before freeing the old one the executor synchronizes the
+ * device).  The block
  * manager, the pools and every per-step array stay the caller's; the manager and
- * the pools must outlive the executor.  pa_step_destroy waits until the executor's
- * last step has finished, then frees what it allocated.  An executor must not be used from two threads at once,
+ * the pools must outlive the executor.  pa_step_destroy synchronizes the executor's
+ * device, then frees what it allocated.  An executor must not be used from two threads at once,
  * and all of its steps must run on one stream (or on streams the caller orders):
  * the device staging buffer is reused by every step.
  *
@@ -146,6 +151,8 @@ typedef struct pa_step_view {
   const int32_t* dev_prefix_lens;
   void* workspace;               /* device workspace of the step's decode */
   size_t workspace_bytes;
+  pa_decode_hints hints;         /* launch hints of the step's pa_decode (seq_order is
+                                    device memory of the executor); unused with groups */
 } pa_step_view;
 
 /* Host and device arrays of the last pa_step_run of this executor, valid until its

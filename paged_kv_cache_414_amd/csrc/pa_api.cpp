@@ -540,6 +540,63 @@ pa_status pa_decode_append(void* out, const void* query, void* key_cache, void* 
                              stream);
 }
 
+}  // extern "C"
+
+namespace pa {
+
+pa_status decode_with_rows(void* out, const void* query, void* key_cache, void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+                           void* workspace, size_t workspace_bytes, const pa_decode_hints* hints,
+                           const void* extra_key, const void* extra_value, const int32_t* extra_slots,
+                           int32_t extra_tokens, void* stream) {
+  DecodePlan plan;
+  pa_status st = plan_decode(&plan, out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                             num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                             scale, dtype, 0, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  st = apply_hints(&plan, hints);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (extra_tokens < 0) return fail(PA_ERR_INVALID_ARG, "extra_tokens %d is negative", extra_tokens);
+  if (extra_tokens > 0) {
+    if (!extra_key || !extra_value || !extra_slots)
+      return fail(PA_ERR_NULL, "extra rows and their slots must not be NULL");
+    if (!aligned16(extra_key) || !aligned16(extra_value))
+      return fail(PA_ERR_INVALID_ARG, "extra rows must be 16-byte aligned");
+    if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+      return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size exceeds the int32 slot range");
+    // rows per workgroup: as many as its threads move in one round of loads and stores
+    // (many small workgroups fill the end of the decode launch; a workgroup looping
+    // over rounds would leave a tail of its own)
+    const int64_t row_chunks = static_cast<int64_t>(num_heads) * (head_dim * static_cast<int64_t>(elem_bytes(dtype)) / 16);
+    const int64_t threads = 64 * static_cast<int64_t>(plan.prm.wide ? pa::kDecodeWavesWide : pa::kDecodeWavesNarrow);
+    int64_t per_group = threads * pa::kExtraChunksPerThread / row_chunks;
+    if (per_group < 1) per_group = 1;
+    if (per_group * row_chunks > INT32_MAX)
+      return fail(PA_ERR_INVALID_ARG, "num_heads * head_dim too large for the extra rows");
+    plan.prm.extra_key = extra_key;
+    plan.prm.extra_value = extra_value;
+    plan.prm.extra_slots = extra_slots;
+    plan.prm.extra_tokens = extra_tokens;
+    plan.prm.extra_per_group = static_cast<int32_t>(per_group);
+    if (static_cast<int64_t>(num_seqs) + pa::extra_slices(plan.prm) > kMaxGridYZ)
+      return fail(PA_ERR_INVALID_ARG, "%d extra rows do not fit the grid after %d sequences", extra_tokens,
+                  num_seqs);
+  }
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = from_hip(pa::launch_decode_partitions(plan.prm, dtype == PA_F16, head_dim, block_size, hs),
+                "decode partition pass launch");
+  if (st != PA_OK) return st;
+  return pa_decode_reduce(out, workspace, workspace_bytes, context_lens, num_seqs, num_heads, head_dim, block_size,
+                          max_context_len, dtype, 0, stream);
+}
+
+}  // namespace pa
+
+extern "C" {
+
 pa_status pa_cache_append(void* key_cache, void* value_cache, const void* key, const void* value,
                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
                           int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,

@@ -334,3 +334,17 @@ pa_status pa_bm_seq_blocks(const pa_block_manager* bm, int64_t seq_id, int32_t* 
 }
 
 }  // extern "C"
+
+namespace pa {
+
+bool batch_shares_blocks(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n) {
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) continue;
+    for (int32_t b : it->second.blocks)
+      if (bm->ref_count[b] > 1) return true;
+  }
+  return false;
+}
+
+}  // namespace pa

@@ -42,6 +42,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #ifndef PA_NONTEMPORAL_KV
 #define PA_NONTEMPORAL_KV 1  // 1: K/V loads carry the non-temporal (streaming) hint
 #endif
+#ifndef PA_KV_BUFFER_AUX
+#define PA_KV_BUFFER_AUX -1  // >= 0: K/V read by buffer loads with this cache-policy word
+#endif
 #ifndef PA_MAX_LOADS_PER_UNIT
 #define PA_MAX_LOADS_PER_UNIT 8  // K (and V) loads per lane for one unit of a block
 #endif
@@ -73,6 +76,19 @@ __device__ __forceinline__ u32x4 load_kv16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 #else
   return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
+
+// Load i of a lane in one unit of a (block, head) chunk: `unit` is the unit's first
+// element (the same in every lane), `elem` this load's element offset in it.
+template <typename T, int kUnitBytes>
+__device__ __forceinline__ u32x4 load_unit16(const T* unit, int elem) {
+#if PA_KV_BUFFER_AUX >= 0
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(unit), 0, kUnitBytes, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, elem * static_cast<int>(sizeof(T)), 0, PA_KV_BUFFER_AUX);
+#else
+  return load_kv16(unit + elem);
 #endif
 }
 
@@ -291,6 +307,7 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
                                              int row, bool active, int n_mine, int n_full,
                                              int tail_valid, float scale_log2, NewRow<T>& nr) {
   using G = Geometry<T, D, BS>;
+  constexpr int kUnitBytes = G::kUnitTok * D * static_cast<int>(sizeof(T));
   for (int base = 0; base < n_mine; base += kWave) {
     if (base > 0) {
       const int idx = base + lane;
@@ -306,17 +323,17 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
       for (int u = 0; u < G::kUnroll; ++u) {
         const int phys = __builtin_amdgcn_readlane(ids, j + u);
         const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j + u) * W, block_stride);
-        const T* kp = k_head + off + lane_off;
 #pragma unroll
-        for (int i = 0; i < G::kLoads; ++i) kr[u][i] = load_kv16(kp + i * G::kTokPerLoad * D);
+        for (int i = 0; i < G::kLoads; ++i)
+          kr[u][i] = load_unit16<T, kUnitBytes>(k_head + off, lane_off + i * G::kTokPerLoad * D);
       }
 #pragma unroll
       for (int u = 0; u < G::kUnroll; ++u) {
         const int phys = __builtin_amdgcn_readlane(ids, j + u);
         const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j + u) * W, block_stride);
-        const T* vp = v_head + off + lane_off;
 #pragma unroll
-        for (int i = 0; i < G::kLoads; ++i) vr[u][i] = load_kv16(vp + i * G::kTokPerLoad * D);
+        for (int i = 0; i < G::kLoads; ++i)
+          vr[u][i] = load_unit16<T, kUnitBytes>(v_head + off, lane_off + i * G::kTokPerLoad * D);
       }
 #pragma unroll
       for (int u = 0; u < G::kUnroll; ++u)
@@ -328,12 +345,12 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
       u32x4 vr[G::kLoads];
       const int phys = __builtin_amdgcn_readlane(ids, j);
       const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * W, block_stride);
-      const T* kp = k_head + off + lane_off;
-      const T* vp = v_head + off + lane_off;
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) kr[i] = load_kv16(kp + i * G::kTokPerLoad * D);
+      for (int i = 0; i < G::kLoads; ++i)
+        kr[i] = load_unit16<T, kUnitBytes>(k_head + off, lane_off + i * G::kTokPerLoad * D);
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) vr[i] = load_kv16(vp + i * G::kTokPerLoad * D);
+      for (int i = 0; i < G::kLoads; ++i)
+        vr[i] = load_unit16<T, kUnitBytes>(v_head + off, lane_off + i * G::kTokPerLoad * D);
       fold_unit<T, D, BS, false>(st, q, kr, vr, scale_log2, row, active, G::kUnitTok);
     }
     // the partly filled last unit of the partition, if this chunk holds it
@@ -342,12 +359,12 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
       u32x4 vr[G::kLoads];
       const int phys = __builtin_amdgcn_readlane(ids, j);
       const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * W, block_stride);
-      const T* kp = k_head + off + lane_off;
-      const T* vp = v_head + off + lane_off;
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) kr[i] = load_kv16(kp + i * G::kTokPerLoad * D);
+      for (int i = 0; i < G::kLoads; ++i)
+        kr[i] = load_unit16<T, kUnitBytes>(k_head + off, lane_off + i * G::kTokPerLoad * D);
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) vr[i] = load_kv16(vp + i * G::kTokPerLoad * D);
+      for (int i = 0; i < G::kLoads; ++i)
+        vr[i] = load_unit16<T, kUnitBytes>(v_head + off, lane_off + i * G::kTokPerLoad * D);
       if (nr.on) {
         // token tail_valid - 1 of this unit is the new one: its registers take the new
         // row, and the lanes of its row will store it into the pools
@@ -422,9 +439,54 @@ __device__ __forceinline__ void store_new_row(const DecodeParams& prm, int seq) 
   }
 }
 
+// Extra rows appended by trailing workgroups of a decode launch: rows [first, first +
+// count) of extra_key / extra_value go to their slots, every head, K and V.  Each
+// thread moves 16-byte chunks, kBatch of them with all loads issued before the
+// stores (the pools and the rows may alias as far as the compiler knows).
+template <typename T, int D, int BS, int kThreads>
+__device__ __forceinline__ void append_extra_rows(const DecodeParams& prm, int first, int count) {
+  constexpr int kChunks = D * static_cast<int>(sizeof(T)) / 16;  // 16-byte chunks per row
+  constexpr int kBatch = kExtraChunksPerThread;
+  const int row_chunks = prm.num_heads * kChunks;
+  const int total = count * row_chunks;
+  const char* src_k = static_cast<const char*>(prm.extra_key);
+  const char* src_v = static_cast<const char*>(prm.extra_value);
+  char* dst_k = static_cast<char*>(const_cast<void*>(prm.key_cache));
+  char* dst_v = static_cast<char*>(const_cast<void*>(prm.value_cache));
+  for (int base = threadIdx.x; base < total; base += kThreads * kBatch) {
+    u32x4 kv[kBatch], vv[kBatch];
+    size_t to[kBatch];
+    bool live[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int idx = base + j * kThreads;
+      live[j] = idx < total;
+      if (!live[j]) continue;
+      const int tok = first + idx / row_chunks;
+      const int r = idx - (idx / row_chunks) * row_chunks;  // head * kChunks + chunk
+      const int slot = prm.extra_slots[tok];
+      live[j] = slot >= 0;
+      if (!live[j]) continue;
+      const int h = r / kChunks;
+      const int c = r - h * kChunks;
+      const size_t from = (static_cast<size_t>(tok) * row_chunks + r) * 16;
+      to[j] = ((static_cast<size_t>(slot / BS) * prm.num_heads + h) * BS + slot % BS) * (D * sizeof(T)) +
+              static_cast<size_t>(c) * 16;
+      kv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src_k + from));
+      vv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src_v + from));
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (!live[j]) continue;
+      store16(dst_k + to[j], kv[j]);
+      store16(dst_v + to[j], vv[j]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // decode, partition pass
-// grid (max partitions, heads, seqs), W wave64s
+// grid (max partitions, heads, seqs + store slices + extra slices), W wave64s
 // ---------------------------------------------------------------------------------
 
 template <typename T, int D, int BS, int W>
@@ -436,10 +498,23 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
   const int part = blockIdx.x;
   const int head = blockIdx.y;
   const int z = blockIdx.z;
-  if (z >= prm.num_seqs) {  // pa_decode_append's store workgroups, one per sequence
-    const int64_t s = (static_cast<int64_t>(z - prm.num_seqs) * prm.num_heads + head) *
-                          prm.num_partitions + part;
-    if (s < prm.num_seqs) store_new_row<T, D, BS, kThreads>(prm, static_cast<int>(s));
+  if (z >= prm.num_seqs) {
+    // store_slices(): one store workgroup per sequence, num_partitions * num_heads a slice
+    const int64_t per_slice = static_cast<int64_t>(prm.num_partitions) * prm.num_heads;
+    const int z_extra =
+        prm.num_seqs + (prm.new_key ? static_cast<int>((prm.num_seqs + per_slice - 1) / per_slice) : 0);
+    if (z < z_extra) {  // pa_decode_append's store workgroups, one per sequence
+      const int64_t s = (static_cast<int64_t>(z - prm.num_seqs) * prm.num_heads + head) *
+                            prm.num_partitions + part;
+      if (s < prm.num_seqs) store_new_row<T, D, BS, kThreads>(prm, static_cast<int>(s));
+    } else {  // workgroups appending the extra rows, extra_per_group each
+      const int64_t g = (static_cast<int64_t>(z - z_extra) * prm.num_heads + head) * prm.num_partitions + part;
+      const int64_t first = g * prm.extra_per_group;
+      if (first < prm.extra_tokens)
+        append_extra_rows<T, D, BS, kThreads>(
+            prm, static_cast<int>(first),
+            static_cast<int>(min(static_cast<int64_t>(prm.extra_per_group), prm.extra_tokens - first)));
+    }
     return;
   }
   // grid slice z decodes sequence z, or seq_order[z] when the caller ordered the launch
@@ -923,11 +998,19 @@ int32_t store_slices(const DecodeParams& prm) {
   return static_cast<int32_t>((prm.num_seqs + per_slice - 1) / per_slice);
 }
 
+// z-slices of the workgroups appending extra rows, extra_per_group rows each
+int32_t extra_slices(const DecodeParams& prm) {
+  if (!prm.extra_key || prm.extra_tokens <= 0 || prm.extra_per_group <= 0) return 0;
+  const int64_t groups = (static_cast<int64_t>(prm.extra_tokens) + prm.extra_per_group - 1) / prm.extra_per_group;
+  const int64_t per_slice = static_cast<int64_t>(prm.num_partitions) * prm.num_heads;
+  return static_cast<int32_t>((groups + per_slice - 1) / per_slice);
+}
+
 template <typename T, int D, int BS>
 static hipError_t launch_partitions_t(const DecodeParams& prm, hipStream_t stream) {
   // pa_decode_append adds z-slices after the last sequence: one workgroup per sequence
   // stores its new rows
-  dim3 grid(prm.num_partitions, prm.num_heads, prm.num_seqs + store_slices(prm));
+  dim3 grid(prm.num_partitions, prm.num_heads, prm.num_seqs + store_slices(prm) + extra_slices(prm));
   if (prm.wide) {
     hipLaunchKernelGGL((decode_partitions_kernel<T, D, BS, kWavesWide>), grid, dim3(kWave * kWavesWide), 0,
                        stream, prm);

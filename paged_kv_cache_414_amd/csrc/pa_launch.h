@@ -19,6 +19,9 @@ namespace pa {
 #endif
 constexpr int kDecodeWavesNarrow = PA_DECODE_WAVES;
 constexpr int kDecodeWavesWide = PA_DECODE_WAVES_WIDE;
+// 16-byte chunks of K (and as many of V) a thread of the decode launch's trailing
+// append workgroups moves with every load issued before the first store
+constexpr int kExtraChunksPerThread = 2;
 
 struct DecodeParams {
   void* out;
@@ -50,6 +53,15 @@ struct DecodeParams {
   // [S] or nullptr: the workgroups of grid slice z decode sequence seq_order[z] (a
   // permutation of the batch), so the caller chooses the dispatch order
   const int32_t* seq_order = nullptr;
+  // Rows appended by trailing workgroups of the same launch (a decode step's admitted
+  // prompts): row i of extra_key / extra_value [extra_tokens, H, D] goes to slot
+  // extra_slots[i] (negative: skipped), extra_per_group rows per workgroup.  The
+  // caller guarantees that no such slot lies in a block this launch reads.
+  const void* extra_key = nullptr;
+  const void* extra_value = nullptr;
+  const int32_t* extra_slots = nullptr;
+  int32_t extra_tokens = 0;
+  int32_t extra_per_group = 0;
 };
 
 // Prefix pass of the shared-prefix decode: one workgroup per (prefix partition,
@@ -114,6 +126,8 @@ struct CopyParams {
 
 // z-slices of store workgroups the partition pass adds for pa_decode_append (0 otherwise)
 int32_t store_slices(const DecodeParams& prm);
+// z-slices of workgroups appending the extra rows (0 without them), after the store slices
+int32_t extra_slices(const DecodeParams& prm);
 hipError_t launch_decode_partitions(const DecodeParams& prm, bool f16, int head_dim,
                                     int block_size, hipStream_t stream);
 hipError_t launch_decode_reduce(const ReduceParams& prm, bool f16, int head_dim,
@@ -123,13 +137,15 @@ hipError_t launch_decode_prefix(const PrefixParams& prm, int head_dim, int block
 hipError_t launch_cache_append(const AppendParams& prm, hipStream_t stream);
 hipError_t launch_block_copy(const CopyParams& prm, hipStream_t stream);
 // bytes / 16 words from `src` (device-visible pinned host memory) to `dst` (device);
-// bytes a multiple of 16, both 16-byte aligned.
-hipError_t launch_stage_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+// bytes a multiple of 16, both 16-byte aligned.  When `flag` (device view of a pinned
+// host word) is given, the kernel writes `step` into it as it starts.
+hipError_t launch_stage_copy(const void* src, void* dst, int64_t bytes, int32_t* flag, int32_t step,
+                             hipStream_t stream);
 // The staging copy and the slot-mapped append of `append` in one launch: the
 // append's slot_mapping is read from the pinned host buffer itself (device view),
-// not from the staged copy being written by the same launch.
+// not from the staged copy being written by the same launch.  `flag` as above.
 hipError_t launch_stage_copy_append(const void* src, void* dst, int64_t bytes, const AppendParams& append,
-                                    hipStream_t stream);
+                                    int32_t* flag, int32_t step, hipStream_t stream);
 
 }  // namespace pa
 

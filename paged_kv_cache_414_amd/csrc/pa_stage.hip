@@ -18,7 +18,17 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void stage_copy_kernel(const u32x4* src, u32x4* dst, int64_t words) {
+// Thread 0 of workgroup 0 first writes `step` into the host word `flag` (when given):
+// a step's staging kernel starts only after the previous step's kernels have finished,
+// so the host learns from it that the previous staging kernel has read its pinned
+// buffer, with no event in the queue.
+__device__ __forceinline__ void mark_started(int32_t* flag, int32_t step) {
+  if (flag && blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<volatile int32_t*>(flag) = step;
+}
+
+__global__ __launch_bounds__(256) void stage_copy_kernel(const u32x4* src, u32x4* dst, int64_t words,
+                                                         int32_t* flag, int32_t step) {
+  mark_started(flag, step);
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
     dst[i] = src[i];
@@ -29,7 +39,9 @@ __global__ __launch_bounds__(256) void stage_copy_kernel(const u32x4* src, u32x4
 // cache_append_kernel does (row i of key/value, head h, to the slot's block and
 // offset), reading each row's slot from the pinned buffer over the host link.
 __global__ __launch_bounds__(256) void stage_copy_append_kernel(const u32x4* src, u32x4* dst, int64_t words,
-                                                                int32_t stage_groups, AppendParams prm) {
+                                                                int32_t stage_groups, AppendParams prm,
+                                                                int32_t* flag, int32_t step) {
+  mark_started(flag, step);
   if (static_cast<int32_t>(blockIdx.x) < stage_groups) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
          i += static_cast<int64_t>(stage_groups) * blockDim.x)
@@ -59,27 +71,28 @@ __global__ __launch_bounds__(256) void stage_copy_append_kernel(const u32x4* src
 
 }  // namespace
 
-hipError_t launch_stage_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+hipError_t launch_stage_copy(const void* src, void* dst, int64_t bytes, int32_t* flag, int32_t step,
+                             hipStream_t stream) {
   const int64_t words = bytes / 16;
-  if (words <= 0) return hipSuccess;
   int64_t groups = (words + 255) / 256;
   if (groups > 64) groups = 64;  // grid-stride beyond 64 x 256 words (256 KiB)
+  if (groups < 1) groups = 1;    // the flag is written even with nothing to copy
   hipLaunchKernelGGL(stage_copy_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0, stream,
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), words);
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), words, flag, step);
   return hipGetLastError();
 }
 
 hipError_t launch_stage_copy_append(const void* src, void* dst, int64_t bytes, const AppendParams& append,
-                                    hipStream_t stream) {
+                                    int32_t* flag, int32_t step, hipStream_t stream) {
   const int64_t words = bytes / 16;
   int64_t stage_groups = (words + 255) / 256;
   if (stage_groups > 64) stage_groups = 64;
   const int64_t threads = static_cast<int64_t>(append.num_tokens) * append.num_heads * (append.row_bytes / 16);
-  const int64_t groups = stage_groups + (threads + 255) / 256;
-  if (groups <= 0) return hipSuccess;
+  int64_t groups = stage_groups + (threads + 255) / 256;
+  if (groups < 1) groups = 1;  // the flag is written even with nothing to copy
   hipLaunchKernelGGL(stage_copy_append_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0, stream,
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), words,
-                     static_cast<int32_t>(stage_groups), append);
+                     static_cast<int32_t>(stage_groups), append, flag, step);
   return hipGetLastError();
 }
 

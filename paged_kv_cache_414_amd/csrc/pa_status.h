@@ -6,6 +6,8 @@
 
 #include "pa.h"
 
+struct pa_block_manager;  // include/pa_blocks.h
+
 namespace pa {
 
 // Record a printf-style message as this thread's last error and return `st`.
@@ -17,6 +19,24 @@ __attribute__((visibility("hidden"))) pa_status clear_error();
 // PA_ERR_UNSUPPORTED with the last error set.
 __attribute__((visibility("hidden"))) pa_status check_dtype_shape(pa_dtype dtype, int32_t head_dim,
                                                                   int32_t block_size);
+
+// True when some block held by one of the listed sequences has a reference count
+// above 1 (held by another sequence too); unknown ids are skipped.
+__attribute__((visibility("hidden"))) bool batch_shares_blocks(const ::pa_block_manager* bm,
+                                                               const int64_t* seq_ids, int32_t n);
+
+// pa_decode_ex whose launch also appends `extra_tokens` rows (extra_key / extra_value
+// [extra_tokens, H, D], device) at extra_slots (device int32, negative: skipped) in
+// trailing workgroups, K and V, bits unchanged.  The caller guarantees that no such
+// slot lies in a block the decode reads (the executor's admitted prompts: their
+// blocks were free before the step).  The pools are written through key_cache /
+// value_cache.
+__attribute__((visibility("hidden"))) pa_status decode_with_rows(
+    void* out, const void* query, void* key_cache, void* value_cache, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
+    void* workspace, size_t workspace_bytes, const pa_decode_hints* hints, const void* extra_key,
+    const void* extra_value, const int32_t* extra_slots, int32_t extra_tokens, void* stream);
 
 }  // namespace pa
 

@@ -51,7 +51,8 @@ class _View(ctypes.Structure):
                 ("block_tables", _p32), ("context_lens", _p32), ("group_starts", _p32),
                 ("prefix_lens", _p32), ("admit_slots", _p32), ("dev_block_tables", _vp),
                 ("dev_context_lens", _vp), ("dev_group_starts", _vp), ("dev_prefix_lens", _vp),
-                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("hints", ops.DecodeHints)]
 
 
 def _host_array(ptr, shape) -> np.ndarray:
@@ -211,9 +212,9 @@ class StepEngine:
                 v.dev_prefix_lens, n, h, d, self.block_size, nb, self.max_blocks_per_seq,
                 v.num_groups, r.max_group_size, r.max_prefix_len, r.max_suffix_len, float(scale),
                 dt, 0, 0, v.workspace, v.workspace_bytes, s)
-        else:
-            status = self._lib.pa_decode(o, q, kc, vc, v.dev_block_tables, v.dev_context_lens, n,
-                                         h, d, self.block_size, nb, self.max_blocks_per_seq,
-                                         r.max_context_len, float(scale), dt, 0, v.workspace,
-                                         v.workspace_bytes, s)
+        else:  # with the step's own launch hints (workgroup size, dispatch order)
+            status = self._lib.pa_decode_ex(o, q, kc, vc, v.dev_block_tables, v.dev_context_lens, n,
+                                            h, d, self.block_size, nb, self.max_blocks_per_seq,
+                                            r.max_context_len, float(scale), dt, 0, v.workspace,
+                                            v.workspace_bytes, ctypes.byref(v.hints), s)
         ops._check(status)

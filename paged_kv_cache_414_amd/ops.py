@@ -19,6 +19,7 @@ LIB_PATH = pathlib.Path(__file__).resolve().with_name("libpa.so")
 PA_F32 = 0
 PA_F16 = 1
 PA_NOALLOC_SCRATCH_BYTES = 32 << 20  # size of pa_decode_noalloc's scratch array (pa.h)
+DECODE_WAVES_NARROW, DECODE_WAVES_WIDE = 8, 16  # the two decode workgroup sizes
 _DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16}
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_INVALID_ARG", 3: "PA_ERR_UNSUPPORTED",
            4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP", 6: "PA_ERR_OUT_OF_BLOCKS"}

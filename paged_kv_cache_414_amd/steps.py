@@ -305,6 +305,10 @@ class StepMix:
     def _finish_record(self, rec: StepRecord) -> None:
         pass
 
+    # the executor's launch hints for pa_decode: 8-wave workgroups, and the longest
+    # contexts first unless the batch's sequences share blocks (include/pa_step.h)
+    ORDER_LONGEST_FIRST = True
+
     def _decode_call(self, k_step, st, tables, ctx, o_tables, o_ctx, max_ctx):
         """The step's decode as a callable of the query (enqueued once per step, and
         again for timing)."""
@@ -312,10 +316,16 @@ class StepMix:
         tables_d = st.device(o_tables, (n, self.mb))
         ctx_d = st.device(o_ctx, (n,))
         ws = self._workspace(n, max_ctx)
+        order_d = None
+        if self.ORDER_LONGEST_FIRST:
+            order_h, o_order = st.take(n)
+            order_h[:] = np.argsort(-np.asarray(ctx), kind="stable")
+            order_d = st.device(o_order, (n,))
 
         def call(q_d):
             ops.pa_decode(self.out, q_d, self.k_cache, self.v_cache, tables_d, ctx_d,
-                          self.scale, max_ctx, 0, ws)
+                          self.scale, max_ctx, 0, ws, seq_order=order_d,
+                          waves=ops.DECODE_WAVES_NARROW)
         return call
 
     def decode_again(self):
@@ -357,16 +367,16 @@ class ContinuousBatching(StepMix):
         return inp
 
     def _host_extra(self, k_step: int, st: Staging):
-        # retire and admit: the decode arrays are already staged, so the blocks of the
-        # finished sequences can be reused by the new prompts, which are written
-        # after the decode in stream order
+        # admit, then retire (as the executor does): the new prompts take only blocks
+        # that were free before this step, and the finished sequences' blocks serve
+        # the next step's admissions
         inp = self.inputs(k_step)
         finishing = inp.finishing
-        for lane in finishing:
-            self.manager.free(int(self.lanes[lane]))
         total = int(inp.prompt_lens.sum())
         pslots_h, o_p = st.take(total + 1)
         ids = self._admit(inp.prompt_lens, pslots_h)
+        for lane in finishing:
+            self.manager.free(int(self.lanes[lane]))
         self.lanes[finishing] = ids
         self._post = pslots_h[:total].copy() if self.keep else None
         pslots_d = st.device(o_p, (total,))
@@ -396,6 +406,8 @@ class SharedPrefix(StepMix):
     With ``shared_decode`` the decode runs through pa_decode_shared_prefix: each
     group's leading blocks that all of its samples still hold are read once for the
     whole group."""
+
+    ORDER_LONGEST_FIRST = False  # the samples share blocks: keep each group together
 
     def __init__(self, seed: int, steps: int | None = None, device="cuda",
                  keep_records=False, shared_decode=False, native=False):

@@ -32,5 +32,6 @@ int main(void) {
   F(pa_step_view, prefix_lens); F(pa_step_view, admit_slots); F(pa_step_view, dev_block_tables);
   F(pa_step_view, dev_context_lens); F(pa_step_view, dev_group_starts);
   F(pa_step_view, dev_prefix_lens); F(pa_step_view, workspace); F(pa_step_view, workspace_bytes);
+  F(pa_step_view, hints);
   return 0;
 }

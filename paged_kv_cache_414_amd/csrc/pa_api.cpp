@@ -68,6 +68,9 @@ pa_status from_hip(hipError_t err, const char* what) {
 // sequences of 16K-32K tokens: 512 workgroups 6.55 TB/s, 4096 workgroups 6.25 TB/s,
 // 256 workgroups 6.52 TB/s, but 4 sequences at 128 workgroups only 5.55 TB/s.
 constexpr int64_t kAutoMinUnits = 512;
+// Workgroups one 1-D launch of the shared-prefix passes may hold (its grid in work-items
+// must fit 32 bits at 512 work-items per workgroup).
+constexpr int64_t kMaxFusedWorkgroups = (int64_t{1} << 32) / 512 - 1;
 constexpr int32_t kAutoMinPartitionTokens = 256;
 constexpr int32_t kMaxGridYZ = 65535;
 
@@ -741,28 +744,25 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_
   float* ws_o = reinterpret_cast<float*>(ws + 2 * ws_align(states * 4));
   const hipStream_t hs = static_cast<hipStream_t>(stream);
 
-  if (num_groups > 0 && plan.NPp > 0) {
-    pa::PrefixParams pp;
-    pp.query = query;
-    pp.key_cache = key_cache;
-    pp.value_cache = value_cache;
-    pp.block_tables = block_tables;
-    pp.group_starts = group_starts;
-    pp.prefix_lens = prefix_lens;
-    pp.ws_m = ws_m;
-    pp.ws_l = ws_l;
-    pp.ws_o = ws_o;
-    pp.num_heads = num_heads;
-    pp.max_blocks_per_seq = max_blocks_per_seq;
-    pp.partition_tokens = plan.Pp;
-    pp.num_partitions = plan.NPp;
-    pp.num_groups = num_groups;
-    pp.query_tiles = plan.QT;
-    pp.slots_per_pair = plan.slots;
-    pp.scale = scale;
-    st = from_hip(pa::launch_decode_prefix(pp, head_dim, block_size, hs), "shared-prefix pass launch");
-    if (st != PA_OK) return st;
-  }
+  const bool prefix_pass = num_groups > 0 && plan.NPp > 0;
+  pa::PrefixParams pp;
+  pp.query = query;
+  pp.key_cache = key_cache;
+  pp.value_cache = value_cache;
+  pp.block_tables = block_tables;
+  pp.group_starts = group_starts;
+  pp.prefix_lens = prefix_lens;
+  pp.ws_m = ws_m;
+  pp.ws_l = ws_l;
+  pp.ws_o = ws_o;
+  pp.num_heads = num_heads;
+  pp.max_blocks_per_seq = max_blocks_per_seq;
+  pp.partition_tokens = plan.Pp;
+  pp.num_partitions = plan.NPp;
+  pp.num_groups = num_groups;
+  pp.query_tiles = plan.QT;
+  pp.slots_per_pair = plan.slots;
+  pp.scale = scale;
 
   pa::DecodeParams dp;
   dp.out = out;
@@ -785,10 +785,6 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_
   dp.prefix_partition_tokens = plan.Pp;
   dp.wide = wide_workgroups(PA_F16, head_dim, block_size, plan.P, num_seqs, num_heads, plan.NPs) ? 1 : 0;
   dp.scale = scale;
-  st = from_hip(pa::launch_decode_partitions(dp, true, head_dim, block_size, hs), "suffix pass launch");
-  if (st != PA_OK) return st;
-  // sequences whose tokens after the prefix fit one partition are finished above
-  if (plan.NPs <= 1) return ok();
 
   pa::ReduceParams rp;
   rp.out = out;
@@ -803,6 +799,32 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_
   rp.prefix_partition_tokens = plan.Pp;
   rp.prefix_slots = plan.NPp;
   rp.slots_per_pair = plan.slots;
+
+#if PA_SHARED_FUSED
+  if (prefix_pass) {
+    // both passes in one launch (8-wave workgroups), every state to the workspace,
+    // then the merge of every (sequence, head)
+    const int64_t groups = static_cast<int64_t>(plan.NPp) * num_heads * num_groups * plan.QT +
+                           static_cast<int64_t>(plan.NPs) * num_heads * num_seqs;
+    if (groups > kMaxFusedWorkgroups)
+      return fail(PA_ERR_INVALID_ARG, "%lld workgroups exceed one launch (%lld)", static_cast<long long>(groups),
+                  static_cast<long long>(kMaxFusedWorkgroups));
+    dp.states_only = 1;
+    dp.wide = 0;
+    st = from_hip(pa::launch_decode_shared_fused(pp, dp, head_dim, block_size, hs), "shared-prefix passes launch");
+    if (st != PA_OK) return st;
+    rp.merge_all = 1;
+    return from_hip(pa::launch_decode_reduce(rp, true, head_dim, hs), "shared-prefix merge launch");
+  }
+#endif
+  if (prefix_pass) {
+    st = from_hip(pa::launch_decode_prefix(pp, head_dim, block_size, hs), "shared-prefix pass launch");
+    if (st != PA_OK) return st;
+  }
+  st = from_hip(pa::launch_decode_partitions(dp, true, head_dim, block_size, hs), "suffix pass launch");
+  if (st != PA_OK) return st;
+  // sequences whose tokens after the prefix fit one partition are finished above
+  if (plan.NPs <= 1) return ok();
   return from_hip(pa::launch_decode_reduce(rp, true, head_dim, hs), "shared-prefix merge launch");
 }
 

@@ -489,15 +489,14 @@ __device__ __forceinline__ void append_extra_rows(const DecodeParams& prm, int f
 // grid (max partitions, heads, seqs + store slices + extra slices), W wave64s
 // ---------------------------------------------------------------------------------
 
+// One workgroup of the partition pass: partition `part` of head `head` of grid slice
+// `z` (a sequence, or one of the trailing store / append slices).
 template <typename T, int D, int BS, int W>
-__global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kernel(DecodeParams prm) {
+__device__ __forceinline__ void partitions_workgroup(const DecodeParams& prm, int part, int head, int z) {
   using G = Geometry<T, D, BS>;
   constexpr int kVec = G::kVec;
   constexpr int kThreads = kWave * W;
 
-  const int part = blockIdx.x;
-  const int head = blockIdx.y;
-  const int z = blockIdx.z;
   if (z >= prm.num_seqs) {
     // store_slices(): one store workgroup per sequence, num_partitions * num_heads a slice
     const int64_t per_slice = static_cast<int64_t>(prm.num_partitions) * prm.num_heads;
@@ -545,7 +544,9 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
   T* out_row = static_cast<T*>(prm.out) + (static_cast<size_t>(seq) * prm.num_heads + head) * D;
 
   if (tok_begin >= ctx) {
-    if (part == 0) {  // no token after `start`: the prefix states alone, or zero
+    // no token after `start`: the prefix states alone, or zero (with states_only the
+    // merge pass writes it)
+    if (part == 0 && !prm.states_only) {
       for (int d = threadIdx.x; d < D; d += kThreads) {
         float m = -INFINITY, l = 0.0f, o = 0.0f;
         if (start > 0) fold_prefix_states(prm, seq, head, start, d, D, m, l, o);
@@ -613,8 +614,9 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
   __syncthreads();
 
   // one partition covers every token after `start`: finish here (merging the
-  // prefix states, if any), no reduce pass needed for this sequence
-  const bool single = ctx - start <= P;
+  // prefix states, if any), no reduce pass needed for this sequence -- unless the
+  // prefix states are written by the same launch (states_only)
+  const bool single = !prm.states_only && ctx - start <= P;
   for (int d = threadIdx.x; d < D; d += kThreads) {
     float m = s_m[0];
 #pragma unroll
@@ -642,6 +644,11 @@ __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kern
   }
 }
 
+template <typename T, int D, int BS, int W>
+__global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kernel(DecodeParams prm) {
+  partitions_workgroup<T, D, BS, W>(prm, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
 // ---------------------------------------------------------------------------------
 // decode, reduce pass: grid (heads, seqs), D threads
 // ---------------------------------------------------------------------------------
@@ -656,7 +663,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(ReduceParams prm) {
   const int Pp = prm.prefix_partition_tokens;
   const int np_suffix = ctx > start ? (ctx - start + P - 1) / P : 0;
   const int np_prefix = start > 0 ? (start + Pp - 1) / Pp : 0;
-  if (np_suffix <= 1) return;  // written directly by the partition pass
+  if (!prm.merge_all && np_suffix <= 1) return;  // written directly by the partition pass
   const int d = threadIdx.x;
   const size_t base = (static_cast<size_t>(seq) * prm.num_heads + head) * prm.slots_per_pair;
   const size_t suffix = base + prm.prefix_slots;
@@ -678,7 +685,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(ReduceParams prm) {
     o = o + prm.ws_o[(suffix + p) * D + d] * f;
   }
   T* out_row = static_cast<T*>(prm.out) + (static_cast<size_t>(seq) * prm.num_heads + head) * D;
-  out_row[d] = Lane16<T>::from_float(o / l);
+  out_row[d] = Lane16<T>::from_float(l > 0.0f ? o / l : 0.0f);  // no state: an empty context
 }
 
 // ---------------------------------------------------------------------------------
@@ -720,10 +727,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define PA_PREFIX_PREFETCH 0
 #endif
 #ifndef PA_PREFIX_WAVES
-#define PA_PREFIX_WAVES 8  // wave64s per prefix workgroup (4 or 8)
+#define PA_PREFIX_WAVES 8  // wave64s per prefix workgroup (4, 8 or 16)
 #endif
 constexpr int kPrefixWaves = PA_PREFIX_WAVES;
-constexpr int kPrefixSlots = 4;  // wave states the LDS merge holds at once
+// wave states the LDS merge holds at once: half the waves park theirs, the other half
+// fold them in (4 waves: all at once)
+constexpr int kPrefixSlots = kPrefixWaves > 4 ? kPrefixWaves / 2 : kPrefixWaves;
 constexpr int kPrefixThreads = kPrefixWaves * kWave;
 static_assert(kPrefixWaves == kPrefixSlots || kPrefixWaves == 2 * kPrefixSlots, "prefix waves");
 constexpr int kTile = 16;  // tokens and queries per matrix-core tile
@@ -744,7 +753,7 @@ template <> struct HalfRun<4> {
 };
 
 template <int D, int BS>
-__global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixParams prm) {
+__device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int part, int head, int zz) {
   static_assert(BS % kTile == 0 && (D == 64 || D == 128), "shape");
   constexpr int kTilesPerBlock = BS / kTile;
   // score product: step c (of kQLoads) gives lane group j the dims
@@ -753,10 +762,8 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
   constexpr int kQLoads = D / 32;
   constexpr int kDv = D / 16;         // dims per lane per V row, also value-product tiles
 
-  const int part = blockIdx.x;
-  const int head = blockIdx.y;
-  const int grp = blockIdx.z / prm.query_tiles;
-  const int qtile = blockIdx.z % prm.query_tiles;  // first tile of 16 queries of this workgroup
+  const int grp = zz / prm.query_tiles;
+  const int qtile = zz % prm.query_tiles;  // first tile of 16 queries of this workgroup
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int c16 = lane % kTile;  // K row and query column of this lane
@@ -986,6 +993,39 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixPar
   }
 }
 
+template <int D, int BS>
+__global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(PrefixParams prm) {
+  prefix_workgroup<D, BS>(prm, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+#if PA_SHARED_FUSED
+// ---------------------------------------------------------------------------------
+// shared-prefix decode in one launch: the prefix pass's workgroups first, then the
+// pass over each sequence's tokens after its prefix, which writes partial states
+// (DecodeParams::states_only) for the merge pass; 1-D grid, kPrefixThreads threads.
+// The prefix workgroups of a batch are few (one per group, query tile, head and
+// prefix partition); launched alone they leave most of the chip's wave slots idle,
+// here the other pass fills them.
+// ---------------------------------------------------------------------------------
+
+template <int D, int BS>
+__global__ __launch_bounds__(kPrefixThreads) void decode_shared_fused_kernel(PrefixParams pp, DecodeParams dp,
+                                                                            int32_t prefix_groups) {
+  static_assert(kPrefixThreads == kWave * kDecodeWavesNarrow, "one workgroup size for both passes");
+  const int i = blockIdx.x;
+  if (i < prefix_groups) {
+    const int np = pp.num_partitions;
+    const int h = pp.num_heads;
+    prefix_workgroup<D, BS>(pp, i % np, (i / np) % h, i / (np * h));
+  } else {
+    const int j = i - prefix_groups;
+    const int np = dp.num_partitions;
+    const int h = dp.num_heads;
+    partitions_workgroup<_Float16, D, BS, kDecodeWavesNarrow>(dp, j % np, (j / np) % h, j / (np * h));
+  }
+}
+#endif  // PA_SHARED_FUSED
+
 // ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
@@ -1101,6 +1141,36 @@ static hipError_t launch_prefix_d(const PrefixParams& prm, int block_size, hipSt
   }
   return hipGetLastError();
 }
+
+#if PA_SHARED_FUSED
+template <int D>
+static hipError_t launch_fused_d(const PrefixParams& pp, const DecodeParams& dp, int block_size,
+                                 hipStream_t stream) {
+  const int64_t prefix_groups =
+      static_cast<int64_t>(pp.num_partitions) * pp.num_heads * pp.num_groups * pp.query_tiles;
+  const int64_t groups = prefix_groups + static_cast<int64_t>(dp.num_partitions) * dp.num_heads * dp.num_seqs;
+  const dim3 grid(static_cast<unsigned>(groups));
+  const int32_t pg = static_cast<int32_t>(prefix_groups);
+  switch (block_size) {
+    case 16: hipLaunchKernelGGL((decode_shared_fused_kernel<D, 16>), grid, dim3(kPrefixThreads), 0, stream, pp, dp, pg); break;
+    case 32: hipLaunchKernelGGL((decode_shared_fused_kernel<D, 32>), grid, dim3(kPrefixThreads), 0, stream, pp, dp, pg); break;
+    case 64: hipLaunchKernelGGL((decode_shared_fused_kernel<D, 64>), grid, dim3(kPrefixThreads), 0, stream, pp, dp, pg); break;
+    case 128: hipLaunchKernelGGL((decode_shared_fused_kernel<D, 128>), grid, dim3(kPrefixThreads), 0, stream, pp, dp, pg); break;
+    case 256: hipLaunchKernelGGL((decode_shared_fused_kernel<D, 256>), grid, dim3(kPrefixThreads), 0, stream, pp, dp, pg); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_shared_fused(const PrefixParams& pp, const DecodeParams& dp, int head_dim, int block_size,
+                                      hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_fused_d<64>(pp, dp, block_size, stream);
+    case 128: return launch_fused_d<128>(pp, dp, block_size, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+#endif  // PA_SHARED_FUSED
 
 hipError_t launch_decode_prefix(const PrefixParams& prm, int head_dim, int block_size,
                                 hipStream_t stream) {

@@ -19,6 +19,10 @@ namespace pa {
 #endif
 constexpr int kDecodeWavesNarrow = PA_DECODE_WAVES;
 constexpr int kDecodeWavesWide = PA_DECODE_WAVES_WIDE;
+#ifndef PA_SHARED_FUSED
+#define PA_SHARED_FUSED 0  // 1: the shared-prefix decode runs both passes in one launch
+#endif
+
 // 16-byte chunks of K (and as many of V) a thread of the decode launch's trailing
 // append workgroups moves with every load issued before the first store
 constexpr int kExtraChunksPerThread = 2;
@@ -62,6 +66,9 @@ struct DecodeParams {
   const int32_t* extra_slots = nullptr;
   int32_t extra_tokens = 0;
   int32_t extra_per_group = 0;
+  // 1: every partition writes its state to the workspace (none finishes a sequence),
+  // for a merge pass with ReduceParams::merge_all; the prefix states may not exist yet
+  int32_t states_only = 0;
 };
 
 // Prefix pass of the shared-prefix decode: one workgroup per (prefix partition,
@@ -100,6 +107,9 @@ struct ReduceParams {
   int32_t prefix_partition_tokens;  // of the prefix states
   int32_t prefix_slots;             // slots [0, prefix_slots) hold prefix states
   int32_t slots_per_pair;
+  // 1: merge and write every (sequence, head), also those with at most one state
+  // after the prefix (zero output for an empty context); 0: only those with more
+  int32_t merge_all = 0;
 };
 
 struct AppendParams {
@@ -134,6 +144,10 @@ hipError_t launch_decode_reduce(const ReduceParams& prm, bool f16, int head_dim,
                                 hipStream_t stream);
 hipError_t launch_decode_prefix(const PrefixParams& prm, int head_dim, int block_size,
                                 hipStream_t stream);
+// The prefix pass (pp) and the pass after the prefix (dp, states_only, 8 waves) in one
+// launch; the caller then merges with launch_decode_reduce (merge_all).
+hipError_t launch_decode_shared_fused(const PrefixParams& pp, const DecodeParams& dp, int head_dim, int block_size,
+                                      hipStream_t stream);
 hipError_t launch_cache_append(const AppendParams& prm, hipStream_t stream);
 hipError_t launch_block_copy(const CopyParams& prm, hipStream_t stream);
 // bytes / 16 words from `src` (device-visible pinned host memory) to `dst` (device);

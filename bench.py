@@ -35,17 +35,17 @@ METRIC = "pa_decode KV GB/s & % of MI355X HBM peak; decode seq-steps/s (1 GPU)"
 # HBM bytes per launch of the step's kernel on this workload (seed 2: the partition
 # pass with the 96 rows' append fused, pa_decode_append), from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
-# known-size block copy (FETCH_SIZE x 1.9987, WRITE_SIZE x 1.000); the commands and
+# known-size block copy (FETCH_SIZE x 1.9987, WRITE_SIZE x 1.0000); the commands and
 # raw values are in profiles/decode_partitions_llama7b_pmc.md.  Valid only for the
 # kernel sources and launch policy they were taken on (sha256 of the kernel file, the
 # launch header whose constants the kernels use, and the host code that picks the
 # partition length and the workgroup size of a launch).
 MEASURED_TRAFFIC = {
-    "kernel_source_sha256": "f7c420fd492260d8b70bc36c081eade59315f289885b29b478e2296e98044607",
+    "kernel_source_sha256": "8e89bf330d75b81b017fd8f75d818f5c433ca17299b2b22408631e95ebb6cbf3",
     "seed": 2,
     "partition_tokens": 2048,
-    "read_bytes": 1940253581,
-    "write_bytes": 2359296,
+    "read_bytes": 1940300190,
+    "write_bytes": 2359234,
 }
 KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                "paged_kv_cache_414_amd", "csrc", name)

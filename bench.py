@@ -91,6 +91,8 @@ def parse():
                     help="also run one pa_block_copy of a known size (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark: pa_decode by block size and head dim")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="instead of the benchmark: the graph-replayed vs eager small-batch steps")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -452,6 +454,7 @@ def graph_step(torch, ops, metrics, args):
             for _ in range(20):
                 fn()
             torch.cuda.synchronize()
+            time.sleep(0.05)  # an idle stretch marks the start of each timed run in a trace
             t0 = time.perf_counter()
             for _ in range(n):
                 fn()
@@ -654,6 +657,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.graph_only:
+        print(json.dumps({"graph_step": graph_step(torch, ops, metrics, args)}), flush=True)
+        return
     if args.sweep:
         from paged_kv_cache_414_amd import sweep
         log(args, "block-size and head-dim sweep")

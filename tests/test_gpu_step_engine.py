@@ -95,8 +95,8 @@ def test_admission_stops_at_the_first_request_that_does_not_fit():
     rng = np.random.default_rng(1)
     for sid, n in ((0, 40), (1, 17)):  # 3 + 2 blocks: 19 free
         _seed_sequence(bm, kc, vc, host, rng, sid, n)
-    # the step's tokens need no new block (positions 40 and 17); sequence 1 then gives
-    # back 2 blocks: 21 free for requests of 7, 10, 1 and 1 blocks
+    # the step's tokens need no new block (positions 40 and 17): 19 free for requests of
+    # 7, 10, 1 and 1 blocks; sequence 1 gives its 2 blocks back after the admissions
     lens = np.array([100, 150, 16, 5], dtype=np.int32)
     total = int(lens.sum())
     pk, pv = _rows(rng, total, 4, 64), _rows(rng, total, 4, 64)
@@ -105,8 +105,9 @@ def test_admission_stops_at_the_first_request_that_does_not_fit():
                          admit_ids=np.array([10, 11, 12, 13]), admit_lens=lens,
                          prompt_k=pk, prompt_v=pv)
     assert res.num_admitted == 4 and v["admit_slots"].size == total
-    # 2 free: the first request (1 block) fits, the second (25) does not, and the
-    # third (1 block) is not admitted although it would fit
+    # 2 free (sequence 1's, given back in the last step): the first request (1 block)
+    # fits, the second (25) does not, and the third (1 block) is not admitted although
+    # it would fit
     lens2 = np.array([16, 400, 5], dtype=np.int32)
     pk2, pv2 = _rows(rng, 421, 4, 64), _rows(rng, 421, 4, 64)
     res2, v2, _, _ = _step(eng, host, rng, [0, 10, 11], 0.125,
@@ -118,6 +119,31 @@ def test_admission_stops_at_the_first_request_that_does_not_fit():
         bm.blocks_of(21)
     with pytest.raises(ValueError):
         bm.blocks_of(22)  # stops at the first that does not fit
+    _pools_equal(kc, vc, host)
+
+
+def test_blocks_given_back_serve_the_next_steps_admissions():
+    """A step's admissions take only blocks that were free before its retirements: the
+    prompt rows are written by the decode's own launch, so they must not land in a
+    block that decode still reads.  A request that fits only with the blocks a finishing
+    sequence gives back waits one step; every decode matches the oracle and the pools
+    match bit for bit."""
+    bm, kc, vc, eng, host = _setup(nb=10, seed=9, mb=16)
+    rng = np.random.default_rng(31)
+    _seed_sequence(bm, kc, vc, host, rng, 0, 40)  # 3 blocks
+    _seed_sequence(bm, kc, vc, host, rng, 1, 90)  # 6 blocks: 1 free
+    assert bm.num_free == 1
+    pk, pv = _rows(rng, 48, 4, 64), _rows(rng, 48, 4, 64)
+    note("step retiring sequence 1 with a 3-block request")
+    res, v, _, _ = _step(eng, host, rng, [0, 1], 0.125, finished=np.array([1]),
+                         admit_ids=np.array([7]), admit_lens=np.array([48], dtype=np.int32),
+                         prompt_k=pk, prompt_v=pv)
+    assert res.num_admitted == 0 and v["admit_slots"].size == 0
+    assert bm.num_free == 7  # sequence 1's 6 blocks are back, after the admissions
+    note("next step: the request fits")
+    res, v, _, _ = _step(eng, host, rng, [0], 0.125, admit_ids=np.array([7]),
+                         admit_lens=np.array([48], dtype=np.int32), prompt_k=pk, prompt_v=pv)
+    assert res.num_admitted == 1 and bm.context_len(7) == 48
     _pools_equal(kc, vc, host)
 
 

@@ -151,11 +151,14 @@ int32_t unit_tokens(pa_dtype dtype, int32_t head_dim, int32_t block_size) {
   return block_size < most ? block_size : most;
 }
 
+// `heads_per_unit` heads share a workgroup (pa::decode_heads_per_unit), so the launch
+// holds num_seqs * num_heads / heads_per_unit * NP workgroups.
 bool wide_workgroups(pa_dtype dtype, int32_t head_dim, int32_t block_size, int32_t P, int32_t num_seqs,
                      int32_t num_heads, int32_t NP) {
   const int32_t unit = unit_tokens(dtype, head_dim, block_size);
   const int64_t units = (static_cast<int64_t>(P) + unit - 1) / unit;
-  const int64_t groups = static_cast<int64_t>(num_seqs) * num_heads * NP;
+  const int32_t hu = pa::decode_heads_per_unit(dtype == PA_F16, head_dim, block_size, num_heads);
+  const int64_t groups = static_cast<int64_t>(num_seqs) * (num_heads / hu) * NP;
   return units >= kWideMinUnits && groups >= kWideMinWorkgroups;
 }
 
@@ -233,6 +236,7 @@ pa_status plan_decode(DecodePlan* plan, void* out, const void* query, const void
   p.slots_per_pair = NP;
   p.slot_offset = 0;
   p.prefix_partition_tokens = P;
+  p.heads_per_unit = pa::decode_heads_per_unit(dtype == PA_F16, head_dim, block_size, num_heads);
   p.wide = wide_workgroups(dtype, head_dim, block_size, P, num_seqs, num_heads, NP) ? 1 : 0;
   p.scale = scale;
   return PA_OK;
@@ -783,6 +787,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_
   dp.slots_per_pair = plan.slots;
   dp.slot_offset = plan.NPp;
   dp.prefix_partition_tokens = plan.Pp;
+  dp.heads_per_unit = pa::decode_heads_per_unit(true, head_dim, block_size, num_heads);
   dp.wide = wide_workgroups(PA_F16, head_dim, block_size, plan.P, num_seqs, num_heads, plan.NPs) ? 1 : 0;
   dp.scale = scale;
 
@@ -811,6 +816,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_
                   static_cast<long long>(kMaxFusedWorkgroups));
     dp.states_only = 1;
     dp.wide = 0;
+    dp.heads_per_unit = 1;
     st = from_hip(pa::launch_decode_shared_fused(pp, dp, head_dim, block_size, hs), "shared-prefix passes launch");
     if (st != PA_OK) return st;
     rp.merge_all = 1;

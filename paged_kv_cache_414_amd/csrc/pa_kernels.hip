@@ -45,6 +45,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #ifndef PA_KV_BUFFER_AUX
 #define PA_KV_BUFFER_AUX -1  // >= 0: K/V read by buffer loads with this cache-policy word
 #endif
+#ifndef PA_HEADS_PER_UNIT
+#define PA_HEADS_PER_UNIT 1  // 2: heads a wave folds per unit when a (block, head) chunk is 4 KiB
+#endif
 #ifndef PA_MAX_LOADS_PER_UNIT
 #define PA_MAX_LOADS_PER_UNIT 8  // K (and V) loads per lane for one unit of a block
 #endif
@@ -199,6 +202,15 @@ struct Geometry {
   // units fetched together per wave: PA_KV_LOADS_IN_FLIGHT 16-byte loads per lane
   static constexpr int kUnroll =
       2 * kLoads >= PA_KV_LOADS_IN_FLIGHT ? 1 : PA_KV_LOADS_IN_FLIGHT / (2 * kLoads);
+  // Heads of one block a wave may fold as one unit (PA_HEADS_PER_UNIT): the chunks of
+  // adjacent heads are adjacent in the pool, so two 4 KiB chunks are one contiguous
+  // 8 KiB run per unit of K (and of V), the run a 32-token block of one head gives.
+  // Measured on MI355X (fp16, 32 heads x 128, the same 96 contexts U[300, 2048]): one
+  // head per unit at block size 16 streams 6.59 TB/s, at block size 32 6.72 TB/s; but
+  // two heads per unit at block size 16 took 351-353 us against 292 us (128 VGPRs and
+  // spilled pointers at 16 waves; half the workgroups), so the default is one.
+  static constexpr int kMaxHeadsPerUnit =
+      (kUnitsPerBlock == 1 && BS * D * static_cast<int>(sizeof(T)) == 4096) ? PA_HEADS_PER_UNIT : 1;
   static_assert(D % kVec == 0 && kLanesPerTok <= kWave, "head_dim");
   static_assert(BS % kUnitTok == 0 && kUnitTok % kTokPerLoad == 0, "block_size");
 };
@@ -281,33 +293,48 @@ __device__ __forceinline__ size_t unit_offset(int phys, int u, size_t block_stri
 
 // The newest token's row when the append is fused into the decode (pa_decode_append).
 // `on` only in the workgroup whose partition ends with that token; the wave that owns
-// the partition's last unit reads the row (k, v: this lane's 16 bytes of it) with that
-// unit's loads and folds it from registers.  The row reaches the pools through a
+// the partition's last unit reads the row (k, v: this lane's 16 bytes of it) in place of
+// the pool slot among that unit's loads.  The row reaches the pools through a
 // workgroup of its own (store_new_row), so no decode workgroup waits on a store.
 template <typename T>
 struct NewRow {
   bool on;
-  const T* k;
+  const T* k;  // this lane's 16 bytes of the first head's row; head j at + j * D
   const T* v;
-  u32x4 nk, nv;
 };
 
-// Fold this wave's units of one (partition, head) into its row state.  The wave
+// Fold this wave's units of one (partition, HU heads) into its row states.  The wave
 // owns units first_unit + j * W (W waves per workgroup), j < n_mine; the first n_full
 // are whole.  Lane j of `ids` holds the physical block of the wave's j-th unit (the
 // first kWave of them); a longer list is fetched kWave at a time from the table.
+// With HU > 1 a unit spans the same tokens of HU adjacent heads, one contiguous run of
+// the pool: loads [j * kLoads, (j + 1) * kLoads) are head j's, folded into st[j] in the
+// same order as with one head per unit, so the result does not depend on HU.
 // With nr.on, the partition's last unit is always folded as the partly filled one
 // and its last live token comes from nr (the same bits the append would have stored,
 // so the result is the same as appending first and decoding after).
-template <typename T, int D, int BS, int W>
-__device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>& st,
-                                             const u32x4& q, int ids, const int* table,
+template <typename T, int D, int BS, int W, int HU>
+__device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec> (&st)[HU],
+                                             const u32x4 (&q)[HU], int ids, const int* table,
                                              int first_unit, const T* k_head, const T* v_head,
                                              size_t block_stride, int lane_off, int lane,
                                              int row, bool active, int n_mine, int n_full,
                                              int tail_valid, float scale_log2, NewRow<T>& nr) {
   using G = Geometry<T, D, BS>;
-  constexpr int kUnitBytes = G::kUnitTok * D * static_cast<int>(sizeof(T));
+  static_assert(HU == 1 || G::kUnitsPerBlock == 1, "heads share a unit only when the unit is the block");
+  constexpr int kL = HU * G::kLoads;  // loads per unit of K (and of V)
+  constexpr int kUnitBytes = HU * G::kUnitTok * D * static_cast<int>(sizeof(T));
+  constexpr int kUnroll = HU == 1 ? G::kUnroll : 1;
+  // element offset of this lane's load i in a unit: head i / kLoads, rows (i % kLoads)
+  auto elem = [&](int i) {
+    return (i / G::kLoads) * (BS * D) + (i % G::kLoads) * G::kTokPerLoad * D + lane_off;
+  };
+  auto fold_whole = [&](const u32x4* kr, const u32x4* vr) {
+#pragma unroll
+    for (int h = 0; h < HU; ++h)
+      fold_unit<T, D, BS, false>(st[h], q[h], kr + h * G::kLoads, vr + h * G::kLoads, scale_log2, row, active,
+                                 G::kUnitTok);
+  };
   for (int base = 0; base < n_mine; base += kWave) {
     if (base > 0) {
       const int idx = base + lane;
@@ -316,77 +343,68 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec>&
     const int chunk_full = min(max(n_full - base, 0), kWave);
     int j = 0;
     // kUnroll whole units per iteration, all loads issued before use
-    for (; j + G::kUnroll <= chunk_full; j += G::kUnroll) {
-      u32x4 kr[G::kUnroll][G::kLoads];
-      u32x4 vr[G::kUnroll][G::kLoads];
+    for (; j + kUnroll <= chunk_full; j += kUnroll) {
+      u32x4 kr[kUnroll][kL];
+      u32x4 vr[kUnroll][kL];
 #pragma unroll
-      for (int u = 0; u < G::kUnroll; ++u) {
+      for (int u = 0; u < kUnroll; ++u) {
         const int phys = __builtin_amdgcn_readlane(ids, j + u);
         const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j + u) * W, block_stride);
 #pragma unroll
-        for (int i = 0; i < G::kLoads; ++i)
-          kr[u][i] = load_unit16<T, kUnitBytes>(k_head + off, lane_off + i * G::kTokPerLoad * D);
+        for (int i = 0; i < kL; ++i) kr[u][i] = load_unit16<T, kUnitBytes>(k_head + off, elem(i));
       }
 #pragma unroll
-      for (int u = 0; u < G::kUnroll; ++u) {
+      for (int u = 0; u < kUnroll; ++u) {
         const int phys = __builtin_amdgcn_readlane(ids, j + u);
         const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j + u) * W, block_stride);
 #pragma unroll
-        for (int i = 0; i < G::kLoads; ++i)
-          vr[u][i] = load_unit16<T, kUnitBytes>(v_head + off, lane_off + i * G::kTokPerLoad * D);
+        for (int i = 0; i < kL; ++i) vr[u][i] = load_unit16<T, kUnitBytes>(v_head + off, elem(i));
       }
 #pragma unroll
-      for (int u = 0; u < G::kUnroll; ++u)
-        fold_unit<T, D, BS, false>(st, q, kr[u], vr[u], scale_log2, row, active, G::kUnitTok);
+      for (int u = 0; u < kUnroll; ++u) fold_whole(kr[u], vr[u]);
     }
     // remaining whole units of this chunk, one at a time
     for (; j < chunk_full; ++j) {
-      u32x4 kr[G::kLoads];
-      u32x4 vr[G::kLoads];
+      u32x4 kr[kL];
+      u32x4 vr[kL];
       const int phys = __builtin_amdgcn_readlane(ids, j);
       const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * W, block_stride);
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i)
-        kr[i] = load_unit16<T, kUnitBytes>(k_head + off, lane_off + i * G::kTokPerLoad * D);
+      for (int i = 0; i < kL; ++i) kr[i] = load_unit16<T, kUnitBytes>(k_head + off, elem(i));
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i)
-        vr[i] = load_unit16<T, kUnitBytes>(v_head + off, lane_off + i * G::kTokPerLoad * D);
-      fold_unit<T, D, BS, false>(st, q, kr, vr, scale_log2, row, active, G::kUnitTok);
+      for (int i = 0; i < kL; ++i) vr[i] = load_unit16<T, kUnitBytes>(v_head + off, elem(i));
+      fold_whole(kr, vr);
     }
     // the partly filled last unit of the partition, if this chunk holds it
     if (n_mine > n_full && base + j == n_full && j < kWave && base + j < n_mine) {
-      u32x4 kr[G::kLoads];
-      u32x4 vr[G::kLoads];
+      u32x4 kr[kL];
+      u32x4 vr[kL];
       const int phys = __builtin_amdgcn_readlane(ids, j);
       const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * W, block_stride);
+      // with nr.on, token tail_valid - 1 of this unit is the new one: the lanes of its
+      // row load it from the new rows (every head of the unit) instead of the pool
+      // slot, which the store workgroups write meanwhile
+      const int r_new = tail_valid - 1;
+      const int i_new = nr.on ? r_new / G::kTokPerLoad : -1;
+      const bool mine = row == r_new % G::kTokPerLoad;
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i)
-        kr[i] = load_unit16<T, kUnitBytes>(k_head + off, lane_off + i * G::kTokPerLoad * D);
-#pragma unroll
-      for (int i = 0; i < G::kLoads; ++i)
-        vr[i] = load_unit16<T, kUnitBytes>(v_head + off, lane_off + i * G::kTokPerLoad * D);
-      if (nr.on) {
-        // token tail_valid - 1 of this unit is the new one: its registers take the new
-        // row, and the lanes of its row will store it into the pools
-        const int r_new = tail_valid - 1;
-        const int i_new = r_new / G::kTokPerLoad;
-        const bool mine = row == r_new % G::kTokPerLoad;
-        if (mine) {
-          nr.nk = load16(nr.k);
-          nr.nv = load16(nr.v);
-        }
-#pragma unroll
-        for (int i = 0; i < G::kLoads; ++i) {
-          if (i == i_new && mine) {
-            kr[i] = nr.nk;
-            vr[i] = nr.nv;
-          }
-        }
+      for (int i = 0; i < kL; ++i) {
+        const bool fresh = i % G::kLoads == i_new && mine;
+        kr[i] = load_kv16(fresh ? nr.k + (i / G::kLoads) * D : k_head + off + elem(i));
       }
-      if (tail_valid == G::kUnitTok)  // only with nr.on: the new token closes its unit,
-        fold_unit<T, D, BS, false>(st, q, kr, vr, scale_log2, row, active, G::kUnitTok);  // folded whole as without it
-      else
-        fold_unit<T, D, BS, true>(st, q, kr, vr, scale_log2, row, active, tail_valid);
+#pragma unroll
+      for (int i = 0; i < kL; ++i) {
+        const bool fresh = i % G::kLoads == i_new && mine;
+        vr[i] = load_kv16(fresh ? nr.v + (i / G::kLoads) * D : v_head + off + elem(i));
+      }
+      if (tail_valid == G::kUnitTok) {  // only with nr.on: the new token closes its unit,
+        fold_whole(kr, vr);             // folded whole as without it
+      } else {
+#pragma unroll
+        for (int h = 0; h < HU; ++h)
+          fold_unit<T, D, BS, true>(st[h], q[h], kr + h * G::kLoads, vr + h * G::kLoads, scale_log2, row, active,
+                                    tail_valid);
+      }
     }
   }
 }
@@ -414,8 +432,8 @@ __device__ __forceinline__ void fold_prefix_states(const DecodeParams& prm, int 
 // z-slices, dispatched after every decode workgroup, so they run in the launch's
 // tail) writes the sequence's new K and V row, every head, into the slot of its position
 // context_lens[seq] - 1.  The decode workgroups fold that row from new_key /
-// new_value, not from the pools: whatever they read in that slot while this
-// workgroup writes it is replaced in registers, so the two never wait on each other.
+// new_value, not from the pools: they never read that slot, so the two never wait
+// on each other.
 // The pools are written only by pa_decode_append, whose caller passes them writable.
 template <typename T, int D, int BS, int kThreads>
 __device__ __forceinline__ void store_new_row(const DecodeParams& prm, int seq) {
@@ -489,25 +507,27 @@ __device__ __forceinline__ void append_extra_rows(const DecodeParams& prm, int f
 // grid (max partitions, heads, seqs + store slices + extra slices), W wave64s
 // ---------------------------------------------------------------------------------
 
-// One workgroup of the partition pass: partition `part` of head `head` of grid slice
-// `z` (a sequence, or one of the trailing store / append slices).
-template <typename T, int D, int BS, int W>
-__device__ __forceinline__ void partitions_workgroup(const DecodeParams& prm, int part, int head, int z) {
+// One workgroup of the partition pass: partition `part` of heads [HU * hg, HU * hg +
+// HU) of grid slice `z` (a sequence, or one of the trailing store / append slices).
+template <typename T, int D, int BS, int W, int HU>
+__device__ __forceinline__ void partitions_workgroup(const DecodeParams& prm, int part, int hg, int z) {
   using G = Geometry<T, D, BS>;
   constexpr int kVec = G::kVec;
   constexpr int kThreads = kWave * W;
+  const int head_groups = prm.num_heads / HU;  // grid y
+  const int head = hg * HU;                    // first head of the workgroup
 
   if (z >= prm.num_seqs) {
     // store_slices(): one store workgroup per sequence, num_partitions * num_heads a slice
-    const int64_t per_slice = static_cast<int64_t>(prm.num_partitions) * prm.num_heads;
+    const int64_t per_slice = static_cast<int64_t>(prm.num_partitions) * head_groups;
     const int z_extra =
         prm.num_seqs + (prm.new_key ? static_cast<int>((prm.num_seqs + per_slice - 1) / per_slice) : 0);
     if (z < z_extra) {  // pa_decode_append's store workgroups, one per sequence
-      const int64_t s = (static_cast<int64_t>(z - prm.num_seqs) * prm.num_heads + head) *
+      const int64_t s = (static_cast<int64_t>(z - prm.num_seqs) * head_groups + hg) *
                             prm.num_partitions + part;
       if (s < prm.num_seqs) store_new_row<T, D, BS, kThreads>(prm, static_cast<int>(s));
     } else {  // workgroups appending the extra rows, extra_per_group each
-      const int64_t g = (static_cast<int64_t>(z - z_extra) * prm.num_heads + head) * prm.num_partitions + part;
+      const int64_t g = (static_cast<int64_t>(z - z_extra) * head_groups + hg) * prm.num_partitions + part;
       const int64_t first = g * prm.extra_per_group;
       if (first < prm.extra_tokens)
         append_extra_rows<T, D, BS, kThreads>(
@@ -538,19 +558,23 @@ __device__ __forceinline__ void partitions_workgroup(const DecodeParams& prm, in
   const int first_unit = unit_begin + wave;
   const int blk0 = (first_unit + lane * W) / G::kUnitsPerBlock;
   const int ids0 = blk0 < prm.max_blocks_per_seq ? table[blk0] : 0;
-  const u32x4 q = load16(static_cast<const T*>(prm.query) +
-                         (static_cast<size_t>(seq) * prm.num_heads + head) * D + col_data * kVec);
+  u32x4 q[HU];
+#pragma unroll
+  for (int h = 0; h < HU; ++h)
+    q[h] = load16(static_cast<const T*>(prm.query) +
+                  (static_cast<size_t>(seq) * prm.num_heads + head + h) * D + col_data * kVec);
   const int ctx = prm.context_lens[seq];
-  T* out_row = static_cast<T*>(prm.out) + (static_cast<size_t>(seq) * prm.num_heads + head) * D;
+  T* out_row = static_cast<T*>(prm.out) + (static_cast<size_t>(seq) * prm.num_heads + head) * D;  // HU rows
 
   if (tok_begin >= ctx) {
     // no token after `start`: the prefix states alone, or zero (with states_only the
     // merge pass writes it)
     if (part == 0 && !prm.states_only) {
-      for (int d = threadIdx.x; d < D; d += kThreads) {
+      for (int e = threadIdx.x; e < HU * D; e += kThreads) {
+        const int d = e % D;
         float m = -INFINITY, l = 0.0f, o = 0.0f;
-        if (start > 0) fold_prefix_states(prm, seq, head, start, d, D, m, l, o);
-        out_row[d] = Lane16<T>::from_float(l > 0.0f ? o / l : 0.0f);
+        if (start > 0) fold_prefix_states(prm, seq, head + e / D, start, d, D, m, l, o);
+        out_row[e] = Lane16<T>::from_float(l > 0.0f ? o / l : 0.0f);
       }
     }
     return;
@@ -580,35 +604,44 @@ __device__ __forceinline__ void partitions_workgroup(const DecodeParams& prm, in
   const int n_full = full_end - unit_begin > wave ? (full_end - unit_begin - wave + W - 1) / W : 0;
   const int tail_valid = tok_end - (first_unit + n_full * W) * G::kUnitTok;
 
-  RowState<kVec> st;
-  st.m = -INFINITY;
-  st.l = 0.0f;
+  RowState<kVec> st[HU];
 #pragma unroll
-  for (int j = 0; j < kVec; ++j) st.acc[j] = 0.0f;
-  attend_units<T, D, BS, W>(st, q, ids0, table, first_unit, k_head, v_head, block_stride, lane_off,
-                            lane, row, active, n_mine, n_full, tail_valid, scale_log2, nr);
+  for (int h = 0; h < HU; ++h) {
+    st[h].m = -INFINITY;
+    st[h].l = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) st[h].acc[j] = 0.0f;
+  }
+  attend_units<T, D, BS, W, HU>(st, q, ids0, table, first_unit, k_head, v_head, block_stride, lane_off,
+                                lane, row, active, n_mine, n_full, tail_valid, scale_log2, nr);
 
-  // merge the token rows of the wave (lanes with the same col)
+  // merge the token rows of the wave (lanes with the same col), each head's in turn
 #pragma unroll
-  for (int off = G::kLanesPerTok; off < kWave; off <<= 1) {
-    const float m_o = __shfl_xor(st.m, off);
-    const float l_o = __shfl_xor(st.l, off);
-    float acc_o[kVec];
+  for (int h = 0; h < HU; ++h) {
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) acc_o[j] = __shfl_xor(st.acc[j], off);
-    merge_state<kVec>(st, m_o, l_o, acc_o);
+    for (int off = G::kLanesPerTok; off < kWave; off <<= 1) {
+      const float m_o = __shfl_xor(st[h].m, off);
+      const float l_o = __shfl_xor(st[h].l, off);
+      float acc_o[kVec];
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) acc_o[j] = __shfl_xor(st[h].acc[j], off);
+      merge_state<kVec>(st[h], m_o, l_o, acc_o);
+    }
   }
 
   // merge the waves through LDS, in wave order
-  __shared__ float s_m[W];
-  __shared__ float s_l[W];
-  __shared__ float s_o[W][D];
+  __shared__ float s_m[HU][W];
+  __shared__ float s_l[HU][W];
+  __shared__ float s_o[HU][W][D];
   if (row == 0 && active) {
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) s_o[wave][col * kVec + j] = st.acc[j];
-    if (col == 0) {
-      s_m[wave] = st.m;
-      s_l[wave] = st.l;
+    for (int h = 0; h < HU; ++h) {
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) s_o[h][wave][col * kVec + j] = st[h].acc[j];
+      if (col == 0) {
+        s_m[h][wave] = st[h].m;
+        s_l[h][wave] = st[h].l;
+      }
     }
   }
   __syncthreads();
@@ -617,23 +650,25 @@ __device__ __forceinline__ void partitions_workgroup(const DecodeParams& prm, in
   // prefix states, if any), no reduce pass needed for this sequence -- unless the
   // prefix states are written by the same launch (states_only)
   const bool single = !prm.states_only && ctx - start <= P;
-  for (int d = threadIdx.x; d < D; d += kThreads) {
-    float m = s_m[0];
+  for (int e = threadIdx.x; e < HU * D; e += kThreads) {
+    const int h = e / D;
+    const int d = e - h * D;
+    float m = s_m[h][0];
 #pragma unroll
-    for (int w = 1; w < W; ++w) m = fmaxf(m, s_m[w]);
+    for (int w = 1; w < W; ++w) m = fmaxf(m, s_m[h][w]);
     float l = 0.0f;
     float o = 0.0f;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const float f = (s_m[w] == -INFINITY) ? 0.0f : fast_exp2(s_m[w] - m);
-      l = l + s_l[w] * f;
-      o = o + s_o[w][d] * f;
+      const float f = (s_m[h][w] == -INFINITY) ? 0.0f : fast_exp2(s_m[h][w] - m);
+      l = l + s_l[h][w] * f;
+      o = o + s_o[h][w][d] * f;
     }
     if (single) {
-      if (start > 0) fold_prefix_states(prm, seq, head, start, d, D, m, l, o);
-      out_row[d] = Lane16<T>::from_float(o / l);
+      if (start > 0) fold_prefix_states(prm, seq, head + h, start, d, D, m, l, o);
+      out_row[e] = Lane16<T>::from_float(o / l);
     } else {
-      const size_t slot = (static_cast<size_t>(seq) * prm.num_heads + head) * prm.slots_per_pair +
+      const size_t slot = (static_cast<size_t>(seq) * prm.num_heads + head + h) * prm.slots_per_pair +
                           prm.slot_offset + part;
       prm.ws_o[slot * D + d] = o;
       if (d == 0) {
@@ -644,9 +679,9 @@ __device__ __forceinline__ void partitions_workgroup(const DecodeParams& prm, in
   }
 }
 
-template <typename T, int D, int BS, int W>
+template <typename T, int D, int BS, int W, int HU>
 __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kernel(DecodeParams prm) {
-  partitions_workgroup<T, D, BS, W>(prm, blockIdx.x, blockIdx.y, blockIdx.z);
+  partitions_workgroup<T, D, BS, W, HU>(prm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1021,7 +1056,7 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_shared_fused_kernel(Pre
     const int j = i - prefix_groups;
     const int np = dp.num_partitions;
     const int h = dp.num_heads;
-    partitions_workgroup<_Float16, D, BS, kDecodeWavesNarrow>(dp, j % np, (j / np) % h, j / (np * h));
+    partitions_workgroup<_Float16, D, BS, kDecodeWavesNarrow, 1>(dp, j % np, (j / np) % h, j / (np * h));
   }
 }
 #endif  // PA_SHARED_FUSED
@@ -1031,10 +1066,10 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_shared_fused_kernel(Pre
 // ---------------------------------------------------------------------------------
 
 // z-slices of store workgroups pa_decode_append adds: one workgroup per sequence,
-// num_partitions * num_heads of them per slice
+// num_partitions * (num_heads / heads_per_unit) of them per slice
 int32_t store_slices(const DecodeParams& prm) {
   if (!prm.new_key || prm.num_seqs == 0) return 0;
-  const int64_t per_slice = static_cast<int64_t>(prm.num_partitions) * prm.num_heads;
+  const int64_t per_slice = static_cast<int64_t>(prm.num_partitions) * (prm.num_heads / prm.heads_per_unit);
   return static_cast<int32_t>((prm.num_seqs + per_slice - 1) / per_slice);
 }
 
@@ -1042,23 +1077,66 @@ int32_t store_slices(const DecodeParams& prm) {
 int32_t extra_slices(const DecodeParams& prm) {
   if (!prm.extra_key || prm.extra_tokens <= 0 || prm.extra_per_group <= 0) return 0;
   const int64_t groups = (static_cast<int64_t>(prm.extra_tokens) + prm.extra_per_group - 1) / prm.extra_per_group;
-  const int64_t per_slice = static_cast<int64_t>(prm.num_partitions) * prm.num_heads;
+  const int64_t per_slice = static_cast<int64_t>(prm.num_partitions) * (prm.num_heads / prm.heads_per_unit);
   return static_cast<int32_t>((groups + per_slice - 1) / per_slice);
+}
+
+template <typename T, int D, int BS, int HU>
+static void launch_partitions_h(const DecodeParams& prm, hipStream_t stream) {
+  // pa_decode_append adds z-slices after the last sequence: one workgroup per sequence
+  // stores its new rows; the executor's extra rows follow
+  dim3 grid(prm.num_partitions, prm.num_heads / HU, prm.num_seqs + store_slices(prm) + extra_slices(prm));
+  if (prm.wide) {
+    hipLaunchKernelGGL((decode_partitions_kernel<T, D, BS, kWavesWide, HU>), grid, dim3(kWave * kWavesWide), 0,
+                       stream, prm);
+  } else {
+    hipLaunchKernelGGL((decode_partitions_kernel<T, D, BS, kWavesNarrow, HU>), grid, dim3(kWave * kWavesNarrow), 0,
+                       stream, prm);
+  }
 }
 
 template <typename T, int D, int BS>
 static hipError_t launch_partitions_t(const DecodeParams& prm, hipStream_t stream) {
-  // pa_decode_append adds z-slices after the last sequence: one workgroup per sequence
-  // stores its new rows
-  dim3 grid(prm.num_partitions, prm.num_heads, prm.num_seqs + store_slices(prm) + extra_slices(prm));
-  if (prm.wide) {
-    hipLaunchKernelGGL((decode_partitions_kernel<T, D, BS, kWavesWide>), grid, dim3(kWave * kWavesWide), 0,
-                       stream, prm);
-  } else {
-    hipLaunchKernelGGL((decode_partitions_kernel<T, D, BS, kWavesNarrow>), grid, dim3(kWave * kWavesNarrow), 0,
-                       stream, prm);
+  constexpr int kMaxHU = Geometry<T, D, BS>::kMaxHeadsPerUnit;
+  if (prm.heads_per_unit != 1 && prm.heads_per_unit != kMaxHU) return hipErrorInvalidValue;
+  if constexpr (kMaxHU > 1) {
+    if (prm.heads_per_unit == kMaxHU) {
+      launch_partitions_h<T, D, BS, kMaxHU>(prm, stream);
+      return hipGetLastError();
+    }
   }
+  launch_partitions_h<T, D, BS, 1>(prm, stream);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static int32_t heads_per_unit_d(int block_size) {
+  switch (block_size) {
+    case 8: return Geometry<T, D, 8>::kMaxHeadsPerUnit;
+    case 16: return Geometry<T, D, 16>::kMaxHeadsPerUnit;
+    case 32: return Geometry<T, D, 32>::kMaxHeadsPerUnit;
+    case 64: return Geometry<T, D, 64>::kMaxHeadsPerUnit;
+    case 128: return Geometry<T, D, 128>::kMaxHeadsPerUnit;
+    case 256: return Geometry<T, D, 256>::kMaxHeadsPerUnit;
+    default: return 1;
+  }
+}
+
+template <typename T>
+static int32_t heads_per_unit_t(int head_dim, int block_size) {
+  switch (head_dim) {
+    case 64: return heads_per_unit_d<T, 64>(block_size);
+    case 80: return heads_per_unit_d<T, 80>(block_size);
+    case 96: return heads_per_unit_d<T, 96>(block_size);
+    case 128: return heads_per_unit_d<T, 128>(block_size);
+    case 256: return heads_per_unit_d<T, 256>(block_size);
+    default: return 1;
+  }
+}
+
+int32_t decode_heads_per_unit(bool f16, int head_dim, int block_size, int num_heads) {
+  const int32_t hu = f16 ? heads_per_unit_t<_Float16>(head_dim, block_size) : heads_per_unit_t<float>(head_dim, block_size);
+  return (hu > 1 && num_heads % hu == 0) ? hu : 1;
 }
 
 template <typename T, int D>

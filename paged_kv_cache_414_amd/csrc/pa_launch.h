@@ -69,6 +69,8 @@ struct DecodeParams {
   // 1: every partition writes its state to the workspace (none finishes a sequence),
   // for a merge pass with ReduceParams::merge_all; the prefix states may not exist yet
   int32_t states_only = 0;
+  // heads one workgroup folds together (decode_heads_per_unit): grid y = num_heads / it
+  int32_t heads_per_unit = 1;
 };
 
 // Prefix pass of the shared-prefix decode: one workgroup per (prefix partition,
@@ -134,6 +136,10 @@ struct CopyParams {
   int64_t block_bytes;  // heads * block_size * head_dim * element size
 };
 
+// Heads a decode workgroup folds per unit for this shape: 2 where a (block, head) chunk
+// is 4 KiB and num_heads is even (the chunks of two adjacent heads are one 8 KiB run),
+// else 1.  The result does not depend on it.
+int32_t decode_heads_per_unit(bool f16, int head_dim, int block_size, int num_heads);
 // z-slices of store workgroups the partition pass adds for pa_decode_append (0 otherwise)
 int32_t store_slices(const DecodeParams& prm);
 // z-slices of workgroups appending the extra rows (0 without them), after the store slices

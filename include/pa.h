@@ -52,6 +52,15 @@
  *    min(max_context_len, max_blocks_per_seq * block_size), distinct non-negative
  *    slots below num_blocks * block_size, and copy pairs whose destinations are
  *    distinct and never a source.  Violations are undefined behaviour.
+ *  * Debug build (libpa_debug.so, compiled with PA_DEBUG_CHECKS=1; pa_debug_checks()
+ *    returns 1): every entry point first waits for the work already on its stream,
+ *    copies the device arrays it is about to hand to a kernel (tables, context
+ *    lengths, slots, copy pairs, dispatch order, groups) to the host and checks every
+ *    precondition stated for them in this header.  A violation returns
+ *    PA_ERR_INVALID_ARG, naming the offending entry in pa_last_error(), before the
+ *    call has enqueued anything.
+ *    The debug build synchronises inside every call, so it cannot be captured into a
+ *    graph and runs slower; results are bit for bit those of the default build.
  *  * Concurrent calls from several host threads are safe; calls that write the same
  *    memory must be ordered by the caller (same stream or events).
  */
@@ -84,6 +93,10 @@ typedef enum pa_status {
 
 /* Version of this ABI (PA_ABI_VERSION of the library that was built). */
 int32_t pa_abi_version(void);
+
+/* 1 in the debug build (device data checked on the host before every launch, as
+ * described above), 0 in the default build. */
+int32_t pa_debug_checks(void);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pa_status_string(pa_status status);

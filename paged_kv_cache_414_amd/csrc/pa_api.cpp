@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdio>
 
+#include "pa_debug.h"
 #include "pa_launch.h"
 #include "pa_status.h"
 
@@ -58,6 +59,16 @@ pa_status from_hip(hipError_t err, const char* what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
+// Builds with PA_DEBUG_CHECKS: the device data a decode launch will read (tables,
+// context lengths, dispatch order), checked on the host; PA_OK otherwise.
+pa_status debug_decode(pa::debug::DecodeView* view, const pa::DecodeParams& p, int32_t num_blocks,
+                       int32_t block_size, int32_t max_context_len, hipStream_t stream) {
+  const pa_status st = pa::debug::decode_data(view, p.block_tables, p.context_lens, p.num_seqs, num_blocks,
+                                              p.max_blocks_per_seq, block_size, max_context_len, stream);
+  if (st != PA_OK) return st;
+  return pa::debug::seq_order(p.seq_order, p.num_seqs, stream);
+}
+
 // Library choice of the partition length: start from the whole longest context
 // (one partition per sequence, no merge pass) and halve while the launch would hold
 // fewer than kAutoMinUnits (sequence, head, partition) workgroups -- two per compute
@@ -68,9 +79,11 @@ pa_status from_hip(hipError_t err, const char* what) {
 // sequences of 16K-32K tokens: 512 workgroups 6.55 TB/s, 4096 workgroups 6.25 TB/s,
 // 256 workgroups 6.52 TB/s, but 4 sequences at 128 workgroups only 5.55 TB/s.
 constexpr int64_t kAutoMinUnits = 512;
+#if PA_SHARED_FUSED
 // Workgroups one 1-D launch of the shared-prefix passes may hold (its grid in work-items
 // must fit 32 bits at 512 work-items per workgroup).
 constexpr int64_t kMaxFusedWorkgroups = (int64_t{1} << 32) / 512 - 1;
+#endif
 constexpr int32_t kAutoMinPartitionTokens = 256;
 constexpr int32_t kMaxGridYZ = 65535;
 
@@ -353,6 +366,8 @@ extern "C" {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
 
+int32_t pa_debug_checks(void) { return PA_DEBUG_CHECKS; }
+
 const char* pa_status_string(pa_status status) {
   switch (status) {
     case PA_OK: return "PA_OK";
@@ -423,6 +438,9 @@ static pa_status decode_partitions_hinted(void* out, const void* query, const vo
   st = apply_hints(&plan, hints);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return ok();
+  pa::debug::DecodeView view;
+  st = debug_decode(&view, plan.prm, num_blocks, block_size, max_context_len, static_cast<hipStream_t>(stream));
+  if (st != PA_OK) return st;
   return from_hip(pa::launch_decode_partitions(plan.prm, dtype == PA_F16, head_dim, block_size,
                                                static_cast<hipStream_t>(stream)),
                   "decode partition pass launch");
@@ -460,6 +478,8 @@ pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_by
     return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   if (!aligned16(out) || !aligned16(workspace))
     return fail(PA_ERR_INVALID_ARG, "out and workspace must be 16-byte aligned");
+  st = pa::debug::lengths(context_lens, num_seqs, max_context_len, static_cast<hipStream_t>(stream));
+  if (st != PA_OK) return st;
   const size_t states = static_cast<size_t>(num_seqs) * num_heads * NP;
   const char* ws = static_cast<const char*>(workspace);
   pa::ReduceParams prm;
@@ -528,6 +548,10 @@ pa_status pa_decode_append_ex(void* out, const void* query, void* key_cache, voi
     return fail(PA_ERR_INVALID_ARG, "num_seqs %d leaves no room for the store workgroups (grid z <= %d)",
                 num_seqs, kMaxGridYZ);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
+  pa::debug::DecodeView view;
+  st = debug_decode(&view, plan.prm, num_blocks, block_size, max_context_len, hs);
+  if (st == PA_OK) st = pa::debug::new_rows(view);
+  if (st != PA_OK) return st;
   st = from_hip(pa::launch_decode_partitions(plan.prm, dtype == PA_F16, head_dim, block_size, hs),
                 "decode partition pass launch");
   if (st != PA_OK) return st;
@@ -593,6 +617,10 @@ pa_status decode_with_rows(void* out, const void* query, void* key_cache, void* 
                   num_seqs);
   }
   const hipStream_t hs = static_cast<hipStream_t>(stream);
+  pa::debug::DecodeView view;
+  st = debug_decode(&view, plan.prm, num_blocks, block_size, max_context_len, hs);
+  if (st == PA_OK && extra_tokens > 0) st = pa::debug::extra_rows(view, extra_slots, extra_tokens, num_blocks, hs);
+  if (st != PA_OK) return st;
   st = from_hip(pa::launch_decode_partitions(plan.prm, dtype == PA_F16, head_dim, block_size, hs),
                 "decode partition pass launch");
   if (st != PA_OK) return st;
@@ -633,6 +661,8 @@ pa_status pa_cache_append(void* key_cache, void* value_cache, const void* key, c
   prm.num_heads = num_heads;
   prm.block_size = block_size;
   prm.row_bytes = row_bytes;
+  st = pa::debug::slots(slot_mapping, num_tokens, num_blocks, block_size, static_cast<hipStream_t>(stream));
+  if (st != PA_OK) return st;
   return from_hip(pa::launch_cache_append(prm, static_cast<hipStream_t>(stream)), "cache append launch");
 }
 
@@ -657,6 +687,8 @@ pa_status pa_block_copy(void* key_cache, void* value_cache, const int32_t* block
   prm.block_pairs = block_pairs;
   prm.num_pairs = num_pairs;
   prm.block_bytes = static_cast<int64_t>(num_heads) * block_size * head_dim * static_cast<int64_t>(elem_bytes(dtype));
+  st = pa::debug::pairs(block_pairs, num_pairs, num_blocks, num_blocks, true, static_cast<hipStream_t>(stream));
+  if (st != PA_OK) return st;
   return from_hip(pa::launch_block_copy(prm, static_cast<hipStream_t>(stream)), "block copy launch");
 }
 
@@ -690,6 +722,9 @@ pa_status pa_swap_blocks(void* dst_key, void* dst_value, const void* src_key, co
   prm.block_pairs = static_cast<const int32_t*>(dev[4]);
   prm.num_pairs = num_pairs;
   prm.block_bytes = static_cast<int64_t>(num_heads) * block_size * head_dim * static_cast<int64_t>(elem_bytes(dtype));
+  st = pa::debug::pairs(block_pairs, num_pairs, src_num_blocks, dst_num_blocks, false,
+                        static_cast<hipStream_t>(stream));
+  if (st != PA_OK) return st;
   return from_hip(pa::launch_block_copy(prm, static_cast<hipStream_t>(stream)), "block swap launch");
 }
 
@@ -747,6 +782,14 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* key_
   float* ws_l = reinterpret_cast<float*>(ws + ws_align(states * 4));
   float* ws_o = reinterpret_cast<float*>(ws + 2 * ws_align(states * 4));
   const hipStream_t hs = static_cast<hipStream_t>(stream);
+  {
+    pa::debug::DecodeView view;
+    st = pa::debug::decode_data(&view, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
+                                block_size, static_cast<int32_t>(row_tokens), hs);
+    if (st == PA_OK)
+      st = pa::debug::groups(view, group_starts, prefix_lens, num_groups, max_prefix_len, max_suffix_len, hs);
+    if (st != PA_OK) return st;
+  }
 
   const bool prefix_pass = num_groups > 0 && plan.NPp > 0;
   pa::PrefixParams pp;

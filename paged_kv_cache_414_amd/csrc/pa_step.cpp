@@ -13,6 +13,7 @@
 #include <new>
 #include <vector>
 
+#include "pa_debug.h"
 #include "pa_launch.h"
 #include "pa_status.h"
 
@@ -372,6 +373,8 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
     ap.num_heads = H;
     ap.block_size = bs;
     ap.row_bytes = D * (c.dtype == PA_F16 ? 2 : 4);
+    st = pa::debug::slots(h + e->off_slots, n, NB, bs, static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
     err = pa::launch_stage_copy_append(e->host_dev[t], e->dev, used_bytes, ap, e->started_dev,
                                        static_cast<int32_t>(e->next_step), static_cast<hipStream_t>(stream));
   } else {

@@ -15,6 +15,8 @@ import pathlib
 import torch
 
 LIB_PATH = pathlib.Path(__file__).resolve().with_name("libpa.so")
+# the same kernels with every entry point checking its device data first (pa.h)
+DEBUG_LIB_PATH = LIB_PATH.with_name("libpa_debug.so")
 
 PA_F32 = 0
 PA_F16 = 1
@@ -28,6 +30,7 @@ _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_INVALID_ARG", 3: "PA_ERR_UNS
 _i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 SIGNATURES = {
     "pa_abi_version": (_i32, []),
+    "pa_debug_checks": (_i32, []),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32]),

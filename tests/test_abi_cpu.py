@@ -42,6 +42,16 @@ def test_library_exports_every_declared_symbol(ops):
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
 
 
+def test_debug_library_exports_every_declared_symbol(ops):
+    """libpa_debug.so: the same kernels and entry points, compiled with PA_DEBUG_CHECKS=1."""
+    dbg = ctypes.CDLL(str(ops.DEBUG_LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(dbg, name), f"{name} declared in include/ but not exported by the debug build"
+    dbg.pa_debug_checks.restype = ctypes.c_int32
+    assert dbg.pa_debug_checks() == 1
+    assert ops.lib.pa_debug_checks() == 0
+
+
 def test_binding_covers_every_declared_symbol(ops):
     assert sorted(ops.SIGNATURES) == declared_functions()
 

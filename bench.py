@@ -337,7 +337,11 @@ def long_context_decode(torch, ops, metrics, args):
         "decode_kv_gbps": round(metrics.gbps(kv, ms * 1e-3), 1),
         "pct_of_hbm_peak": round(100.0 * metrics.gbps(kv, ms * 1e-3) / metrics.HBM_PEAK_GBPS, 2),
         "partition_pass_ms": round(ms_part, 5),
+        "reduce_ms": round(ms - ms_part, 5),
         "seq_steps_per_s": round(b.num_seqs / (ms * 1e-3), 1),
+        "besides_kv": metrics.side_counts(b.context_lens, b.num_heads, b.head_dim, 2, b.block_tables.shape[1],
+                                          ops.pa_decode_num_partitions(b.num_seqs, b.num_heads, b.block_size,
+                                                                       b.max_context_len)),
         "decode_launch_ms": spread,
     }
 
@@ -759,6 +763,8 @@ def main():
                                         "kv_gbps": round(achieved_alone, 2),
                                         "frac": round(achieved_alone / metrics.HBM_PEAK_GBPS, 4)},
         "kv_bytes_per_step": kv,
+        "besides_kv": metrics.side_counts(ctx, h_count, d, batch.q.itemsize, batch.block_tables.shape[1],
+                                          n_parts),
         "roofline": {
             "kernel": (f"decode_partitions_kernel<f16, 128, 16>, {waves} waves per workgroup, "
                        "with the append fused (pa_decode_append)"),

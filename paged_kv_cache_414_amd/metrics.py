@@ -40,6 +40,27 @@ def decode_flops(context_lens, heads: int, head_dim: int) -> int:
     return 4 * total_tokens * int(heads) * int(head_dim)
 
 
+def side_counts(context_lens, heads: int, head_dim: int, elem_bytes: int,
+                max_blocks_per_seq: int, num_partitions: int) -> dict:
+    """What a decode call moves or computes besides the K and V rows: q read and the
+    output written (S x H x D elements each), the block table and context lengths
+    read (int32), the partition states written and read back when the call splits the
+    contexts (m, l and o in float32 per (sequence, head, partition)), the flops of
+    :func:`decode_flops` and one exponential per (token, head)."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    s, h, d = len(ctx), int(heads), int(head_dim)
+    total = int(ctx.sum())
+    np_ = int(num_partitions)
+    return {
+        "q_bytes": s * h * d * int(elem_bytes),
+        "out_bytes": s * h * d * int(elem_bytes),
+        "table_bytes": s * int(max_blocks_per_seq) * 4 + s * 4,
+        "workspace_bytes": 2 * s * h * np_ * (d + 2) * 4 if np_ > 1 else 0,
+        "flops": decode_flops(ctx, h, d),
+        "transcendentals": total * h,
+    }
+
+
 def append_bytes(num_tokens: int, heads: int, head_dim: int, elem_bytes: int) -> int:
     """Read and write of the appended K and V rows."""
     return 2 * 2 * int(num_tokens) * int(heads) * int(head_dim) * int(elem_bytes)

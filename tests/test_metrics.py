@@ -34,3 +34,15 @@ def test_fused_append_adds_only_the_written_rows():
     # the live rows the decode bytes already count)
     assert metrics.fused_append_bytes(96, 32, 128, 2) == 96 * 16384
     assert metrics.append_bytes(96, 32, 128, 2) == 2 * metrics.fused_append_bytes(96, 32, 128, 2)
+
+
+def test_side_counts_of_a_decode_call():
+    """q, output, table and partition-state bytes, flops and exponentials beside the KV
+    rows, written out for 2 sequences x 3 heads x 4 dims, 5 table entries per row."""
+    from paged_kv_cache_414_amd import metrics
+    one = metrics.side_counts([3, 7], 3, 4, 2, 5, 1)
+    assert one == {"q_bytes": 48, "out_bytes": 48, "table_bytes": 48, "workspace_bytes": 0,
+                   "flops": 480, "transcendentals": 30}
+    # three partitions: m and l (one float each) and o (4 floats) per (seq, head,
+    # partition), written by the partition pass and read back by the merge
+    assert metrics.side_counts([3, 7], 3, 4, 2, 5, 3)["workspace_bytes"] == 2 * (2 * 3 * 3) * 6 * 4

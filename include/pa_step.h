@@ -20,20 +20,25 @@
  *      back: a block given back in a step goes to new requests from the next step on,
  *      so no prompt row of a step lands in a block that step's decode reads;
  *   4. every small array the device needs is written into a pinned host buffer of
- *      the executor and moved to the device by one small kernel that reads that
- *      buffer, on `stream` (so the kernels that follow wait on no DMA engine);
- *   5. on `stream`: pa_block_copy when copy-on-write pairs are due, pa_cache_append
- *      of the step's new K/V rows (in the staging launch when no copy is due), then
- *      the decode.  Without groups the decode is pa_decode_ex, whose launch also writes
- *      the admitted prompts' rows in trailing workgroups, with 8-wave workgroups and,
- *      unless some block of the batch is held by several sequences, the longest
- *      contexts dispatched first; with groups it is pa_decode_shared_prefix followed by
- *      pa_cache_append of the prompts' rows.
+ *      the executor (device-mapped, one of two used in turn);
+ *   5. without copy-on-write due and without groups, the step is one launch on
+ *      `stream`: the decode (8-wave workgroups, batch order) reads the arrays from
+ *      the pinned buffer itself, attends each sequence's new row from new_key /
+ *      new_value and stores it, and writes the admitted prompts' rows, in trailing
+ *      workgroups (pa_decode_append_ex with prompt rows).  Otherwise one small kernel
+ *      on `stream` copies the arrays into a device buffer (so the kernels that follow
+ *      wait on no DMA engine), then: pa_block_copy when copy-on-write pairs are due,
+ *      pa_cache_append of the step's new K/V rows (in the staging launch when no copy
+ *      is due), and the decode: without groups pa_decode_ex with the prompts' rows in
+ *      trailing workgroups, 8-wave workgroups and, unless some block of the batch is
+ *      held by several sequences, the longest contexts dispatched first; with groups
+ *      pa_decode_shared_prefix followed by pa_cache_append of the prompts' rows.
  *
  * Ownership.  Unlike the entry points of pa.h, an executor allocates: two pinned
- * host staging buffers, a pinned host word into which each step's staging kernel
- * writes its step number as it starts (the host reuses a staging buffer once the step
- * after the one that read it has started: no event is recorded per step), one device
+ * host staging buffers, a pinned host word into which each step's first launch (the
+ * one-launch decode, or the staging kernel) writes its step number as it starts (the
+ * host reuses a staging buffer once the step after the one that read it has started:
+ * no event is recorded per step), one device
  * staging buffer (sized at creation) and a device workspace for the decode (grown
  * when a step needs more; before freeing the old one the executor synchronizes the
  * device).  The block
@@ -41,7 +46,7 @@
  * the pools must outlive the executor.  pa_step_destroy synchronizes the executor's
  * device, then frees what it allocated.  An executor must not be used from two threads at once,
  * and all of its steps must run on one stream (or on streams the caller orders):
- * the device staging buffer is reused by every step.
+ * the staging buffers are reused from step to step.
  *
  * Errors follow pa.h (status codes, pa_last_error()).
  */
@@ -145,7 +150,8 @@ typedef struct pa_step_view {
   const int32_t* group_starts;   /* host [num_groups + 1], or NULL */
   const int32_t* prefix_lens;    /* host [num_seqs] (tokens), or NULL */
   const int32_t* admit_slots;    /* host [admitted_tokens]: the prompts' slots */
-  const int32_t* dev_block_tables;  /* device copies of the arrays above */
+  const int32_t* dev_block_tables;  /* the arrays above as the step's kernels read them:
+                                       the device copy, or the pinned buffer itself */
   const int32_t* dev_context_lens;
   const int32_t* dev_group_starts;
   const int32_t* dev_prefix_lens;

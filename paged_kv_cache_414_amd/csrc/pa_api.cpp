@@ -581,7 +581,8 @@ pa_status decode_with_rows(void* out, const void* query, void* key_cache, void* 
                            int32_t max_blocks_per_seq, int32_t max_context_len, float scale, pa_dtype dtype,
                            void* workspace, size_t workspace_bytes, const pa_decode_hints* hints,
                            const void* extra_key, const void* extra_value, const int32_t* extra_slots,
-                           int32_t extra_tokens, void* stream) {
+                           int32_t extra_tokens, const void* new_key, const void* new_value,
+                           int32_t* started_flag, int32_t step, void* stream) {
   DecodePlan plan;
   pa_status st = plan_decode(&plan, out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
                              num_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
@@ -590,6 +591,15 @@ pa_status decode_with_rows(void* out, const void* query, void* key_cache, void* 
   st = apply_hints(&plan, hints);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return ok();
+  if (!new_key != !new_value) return fail(PA_ERR_NULL, "new_key and new_value go together");
+  if (new_key) {
+    if (!aligned16(new_key) || !aligned16(new_value))
+      return fail(PA_ERR_INVALID_ARG, "new_key and new_value must be 16-byte aligned");
+    plan.prm.new_key = new_key;
+    plan.prm.new_value = new_value;
+  }
+  plan.prm.started_flag = started_flag;
+  plan.prm.step = step;
   if (extra_tokens < 0) return fail(PA_ERR_INVALID_ARG, "extra_tokens %d is negative", extra_tokens);
   if (extra_tokens > 0) {
     if (!extra_key || !extra_value || !extra_slots)
@@ -612,13 +622,14 @@ pa_status decode_with_rows(void* out, const void* query, void* key_cache, void* 
     plan.prm.extra_slots = extra_slots;
     plan.prm.extra_tokens = extra_tokens;
     plan.prm.extra_per_group = static_cast<int32_t>(per_group);
-    if (static_cast<int64_t>(num_seqs) + pa::extra_slices(plan.prm) > kMaxGridYZ)
-      return fail(PA_ERR_INVALID_ARG, "%d extra rows do not fit the grid after %d sequences", extra_tokens,
-                  num_seqs);
   }
+  if (static_cast<int64_t>(num_seqs) + pa::store_slices(plan.prm) + pa::extra_slices(plan.prm) > kMaxGridYZ)
+    return fail(PA_ERR_INVALID_ARG, "%d extra rows and the new rows do not fit the grid after %d sequences",
+                extra_tokens, num_seqs);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   pa::debug::DecodeView view;
   st = debug_decode(&view, plan.prm, num_blocks, block_size, max_context_len, hs);
+  if (st == PA_OK && new_key) st = pa::debug::new_rows(view);
   if (st == PA_OK && extra_tokens > 0) st = pa::debug::extra_rows(view, extra_slots, extra_tokens, num_blocks, hs);
   if (st != PA_OK) return st;
   st = from_hip(pa::launch_decode_partitions(plan.prm, dtype == PA_F16, head_dim, block_size, hs),

@@ -681,6 +681,9 @@ __device__ __forceinline__ void partitions_workgroup(const DecodeParams& prm, in
 
 template <typename T, int D, int BS, int W, int HU>
 __global__ __launch_bounds__(kWave * W) PA_OCCUPANCY void decode_partitions_kernel(DecodeParams prm) {
+  // the executor learns from this word that the previous step's launches are done
+  if (prm.started_flag && (blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0)
+    *reinterpret_cast<volatile int32_t*>(prm.started_flag) = prm.step;
   partitions_workgroup<T, D, BS, W, HU>(prm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 

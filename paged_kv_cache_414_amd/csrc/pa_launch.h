@@ -71,6 +71,11 @@ struct DecodeParams {
   int32_t states_only = 0;
   // heads one workgroup folds together (decode_heads_per_unit): grid y = num_heads / it
   int32_t heads_per_unit = 1;
+  // The decode-step executor's word (device view of pinned host memory) into which
+  // thread 0 of the launch's first workgroup writes `step` as the launch starts, or
+  // nullptr
+  int32_t* started_flag = nullptr;
+  int32_t step = 0;
 };
 
 // Prefix pass of the shared-prefix decode: one workgroup per (prefix partition,

@@ -33,6 +33,20 @@ bool step_started(const int32_t* word, uint32_t step) {
   return static_cast<int32_t>(seen - step) >= 0;
 }
 
+// One-launch steps (see step 4 of pa_step_run), and whether they keep the longest-first
+// dispatch order.  Measured on MI355X, the same box, interleaved builds, wall clock of
+// the warm mixes (seq.steps/s): continuous batching 794-803K through the staging
+// kernel, 801-805K in one launch with the longest-first order (each workgroup first
+// reads its slot of the order from the pinned buffer, one more dependent trip over
+// the host link), 817-823K in one launch in batch order; the shared-prefix mix through
+// pa_decode 615-616K staged, 627-636K in one launch.
+#ifndef PA_STEP_DIRECT
+#define PA_STEP_DIRECT 1  // 0: every step's arrays go through the staging kernel
+#endif
+#ifndef PA_STEP_DIRECT_ORDER
+#define PA_STEP_DIRECT_ORDER 0  // 1: one-launch steps keep the longest-first order
+#endif
+
 // How long the host polls the word before it falls back to synchronizing the stream.
 constexpr auto kPollFor = std::chrono::milliseconds(5);
 
@@ -87,6 +101,7 @@ struct pa_step_engine {
   int32_t last_groups = 0;
   pa_step_result last{};
   pa_decode_hints last_hints{};
+  bool last_direct = false;  // the last step's decode read the pinned buffer itself
 
   ~pa_step_engine() {
     // the device may still run the last step, reading the staging buffers and the
@@ -347,22 +362,42 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
   // 8 samples sharing 1024 tokens: 108.3 us against 122.1 with 16 waves; longest first
   // 161 us, it splits the groups); other batches with 8 waves and the longest contexts
   // dispatched first (64 x U[1, 562]: 43.1 us against 44.7 with the library's choice;
-  // the Llama-shaped batch the same within 0.2 %).
+  // the Llama-shaped batch the same within 0.2 %).  That order costs one-launch steps
+  // more than it gains, so they keep batch order (PA_STEP_DIRECT_ORDER).
   pa_decode_hints hints{};
   hints.waves = pa::kDecodeWavesNarrow;
-  if (g_count == 0 && !pa::batch_shares_blocks(e->bm, a->seq_ids, n)) {
+  const bool longest_first = g_count == 0 && !pa::batch_shares_blocks(e->bm, a->seq_ids, n);
+  if (longest_first) {
     int32_t* order = h + e->off_order;
     for (int32_t i = 0; i < n; ++i) order[i] = i;
     std::stable_sort(order, order + n, [ctx](int32_t x, int32_t y) { return ctx[x] > ctx[y]; });
-    hints.seq_order = e->dev_at(e->off_order);
   }
 
-  // ---- 4. one copy of the staged arrays, by a kernel on the step's stream; with no
-  // copy-on-write due, the append of the step's rows runs in the same launch ----
+  // ---- 4. the staged arrays reach the device.  Without copy-on-write and groups the
+  // step is one launch: the decode reads them from the pinned buffer itself, attends
+  // the step's new rows from new_key / new_value and stores them and the admitted
+  // prompts' rows in trailing workgroups.  Otherwise a kernel on the step's stream
+  // copies them (with no copy-on-write due, the append of the step's rows rides in
+  // that launch). ----
   const int32_t H = c.num_heads, D = c.head_dim, NB = e->num_blocks;
   const int64_t used = aligned(admitted_tokens > 0 ? e->off_admit + admitted_tokens : e->off_admit);
   const int64_t used_bytes = used * static_cast<int64_t>(sizeof(int32_t));
-  if (copies == 0) {
+  const bool direct = PA_STEP_DIRECT && copies == 0 && g_count == 0;
+  const int32_t* staged = direct ? static_cast<const int32_t*>(e->host_dev[t]) : e->dev;  // as the device reads
+  if (longest_first && (PA_STEP_DIRECT_ORDER || !direct)) hints.seq_order = staged + e->off_order;
+  const int32_t this_step = static_cast<int32_t>(e->next_step);
+  // once the launch that starts the step (and writes its number into the pinned word)
+  // is enqueued, buffer t is in use until that word shows the next step
+  auto mark_used = [e, t]() {
+    e->used[t] = true;
+    e->used_by[t] = e->next_step++;
+    e->any_step = true;
+    e->turn ^= 1;
+  };
+  err = hipSuccess;
+  if (direct) {
+    // the decode launch below marks the step started
+  } else if (copies == 0) {
     pa::AppendParams ap;
     ap.key_cache = e->key_cache;
     ap.value_cache = e->value_cache;
@@ -382,10 +417,7 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
                                 static_cast<int32_t>(e->next_step), static_cast<hipStream_t>(stream));
   }
   if (err != hipSuccess) return hip_fail(err, "pa_step_run: staging copy");
-  e->used[t] = true;
-  e->used_by[t] = e->next_step++;
-  e->any_step = true;
-  e->turn ^= 1;
+  if (!direct) mark_used();
 
   // ---- 5. kernels, in stream order ----
   const size_t need_ws =
@@ -425,12 +457,16 @@ pa_status pa_step_run(pa_step_engine* e, const pa_step_args* a, void* stream, pa
     }
   } else {
     // the admitted prompts' rows are written by trailing workgroups of the decode launch
-    st = pa::decode_with_rows(a->out, a->query, e->key_cache, e->value_cache, e->dev_at(e->off_tables),
-                              e->dev_at(e->off_ctx), n, H, D, bs, NB, mb, max_ctx, a->scale, c.dtype, e->workspace,
-                              e->workspace_bytes, &hints, a->prompt_key, a->prompt_value, e->dev_at(e->off_admit),
-                              static_cast<int32_t>(admitted_tokens), stream);
+    st = pa::decode_with_rows(a->out, a->query, e->key_cache, e->value_cache, staged + e->off_tables,
+                              staged + e->off_ctx, n, H, D, bs, NB, mb, max_ctx, a->scale, c.dtype, e->workspace,
+                              e->workspace_bytes, &hints, a->prompt_key, a->prompt_value, staged + e->off_admit,
+                              static_cast<int32_t>(admitted_tokens), direct ? a->new_key : nullptr,
+                              direct ? a->new_value : nullptr, direct ? e->started_dev : nullptr, this_step,
+                              stream);
     if (st != PA_OK) return st;
+    if (direct) mark_used();
   }
+  e->last_direct = direct;
 
   pa_step_result r{};
   r.num_copies = copies;
@@ -466,10 +502,11 @@ pa_status pa_step_last(const pa_step_engine* e, pa_step_view* v) {
   v->group_starts = grouped ? h + e->off_starts : nullptr;
   v->prefix_lens = grouped ? h + e->off_prefix : nullptr;
   v->admit_slots = h + e->off_admit;
-  v->dev_block_tables = e->dev_at(e->off_tables);
-  v->dev_context_lens = e->dev_at(e->off_ctx);
-  v->dev_group_starts = grouped ? e->dev_at(e->off_starts) : nullptr;
-  v->dev_prefix_lens = grouped ? e->dev_at(e->off_prefix) : nullptr;
+  const int32_t* dev = e->last_direct ? static_cast<const int32_t*>(e->host_dev[e->last_turn]) : e->dev;
+  v->dev_block_tables = dev + e->off_tables;
+  v->dev_context_lens = dev + e->off_ctx;
+  v->dev_group_starts = grouped ? dev + e->off_starts : nullptr;
+  v->dev_prefix_lens = grouped ? dev + e->off_prefix : nullptr;
   v->workspace = e->workspace;
   v->workspace_bytes = e->workspace_bytes;
   v->hints = e->last_hints;

@@ -248,6 +248,27 @@ def test_groups_with_empty_and_single_members_and_decode_again():
     _pools_equal(kc, vc, host)
 
 
+def test_one_launch_steps_and_decode_again():
+    """Steps with no copy-on-write and no groups are one decode launch that reads the
+    staged arrays from the pinned buffer; the view exposes that buffer, and the decode
+    enqueued again from it reproduces the step's output bit for bit."""
+    bm, kc, vc, eng, host = _setup(nb=200, h=4, bs=16, d=64, seed=9, max_seqs=8, mb=20, admit=0)
+    rng = np.random.default_rng(7)
+    for sid, n in ((0, 70), (1, 15), (2, 16), (3, 1)):
+        _seed_sequence(bm, kc, vc, host, rng, sid, n)
+    ids = [0, 1, 2, 3]
+    for step in range(4):
+        note(f"one-launch step {step}")
+        res, view, out, q = _step(eng, host, rng, ids, 0.125)
+        assert res.num_copies == 0
+        first = out.clone()
+        out.zero_()
+        eng.decode_again(dev(q), out, 0.125)
+        torch.cuda.synchronize()
+        assert torch.equal(out, first)
+    _pools_equal(kc, vc, host)
+
+
 RANDOM_SHAPES = [
     # dtype, heads, block size, head dim, seed
     (np.float16, 2, 16, 64, 23),

@@ -135,8 +135,8 @@ def launch_spread(fn, n, torch):
             "p90_ms": round(float(p90), 5)}
 
 
-# Worker processes the multi-core leg of the CPU baseline may use: the CPU share of a
-# one-GPU machine, whatever more the affinity mask shows.
+# Worker processes the multi-core leg of the CPU baseline may use at most: the host cores
+# a one-GPU node of an MI355X machine provides (16), whatever more the affinity mask shows.
 CPU_POOL_LIMIT = 16
 
 

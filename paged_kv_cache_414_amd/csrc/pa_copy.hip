@@ -55,7 +55,7 @@ constexpr int kAppendThreads = 256;
 // read by a decode, which streams them from HBM.  Measured on MI355X (4,096 prompt rows
 // into 256 whole blocks, 134 MB read + written): 26.1 us streaming against 27.2-27.4 us
 // with plain loads and stores; moving 2 or 4 tokens per thread with every load issued
-// first was slower (29.5-31.2 us).  (Block copy, same box: 8 or 2 chunks per thread
+// first was slower (29.5-31.2 us).  (Block copy, same machine: 8 or 2 chunks per thread
 // instead of 4, or 256 threads per workgroup, measured no faster.)
 #ifndef PA_APPEND_STREAM
 #define PA_APPEND_STREAM 1

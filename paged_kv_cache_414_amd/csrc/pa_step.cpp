@@ -34,7 +34,7 @@ bool step_started(const int32_t* word, uint32_t step) {
 }
 
 // One-launch steps (see step 4 of pa_step_run), and whether they keep the longest-first
-// dispatch order.  Measured on MI355X, the same box, interleaved builds, wall clock of
+// dispatch order.  Measured on one MI355X, interleaved builds, wall clock of
 // the warm mixes (seq.steps/s): continuous batching 794-803K through the staging
 // kernel, 801-805K in one launch with the longest-first order (each workgroup first
 // reads its slot of the order from the pinned buffer, one more dependent trip over

@@ -229,7 +229,7 @@ def _draw_shared_case(i):
     return d, bs, sizes, (plo, phi), (slo, shi), ungrouped, part, ppart, mgs
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(48))
 def test_random_shared_prefix_layouts(i):
     """Seeded random group layouts, block sizes, prefix and suffix lengths, partition
     lengths of both passes, and max_group_size given or left to the library."""

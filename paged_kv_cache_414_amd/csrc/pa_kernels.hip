@@ -383,19 +383,24 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec> 
       const size_t off = unit_offset<T, D, BS>(phys, first_unit + (base + j) * W, block_stride);
       // with nr.on, token tail_valid - 1 of this unit is the new one: the lanes of its
       // row load it from the new rows (every head of the unit) instead of the pool
-      // slot, which the store workgroups write meanwhile
+      // slot, which the store workgroups write meanwhile.  The lanes of rows past the
+      // last live token load nothing (the fold below never uses those registers), so
+      // the slots past the context cost no HBM traffic.
       const int r_new = tail_valid - 1;
       const int i_new = nr.on ? r_new / G::kTokPerLoad : -1;
       const bool mine = row == r_new % G::kTokPerLoad;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < kL; ++i) {
         const bool fresh = i % G::kLoads == i_new && mine;
-        kr[i] = load_kv16(fresh ? nr.k + (i / G::kLoads) * D : k_head + off + elem(i));
+        const bool live = (i % G::kLoads) * G::kTokPerLoad + row < tail_valid;
+        kr[i] = live ? load_kv16(fresh ? nr.k + (i / G::kLoads) * D : k_head + off + elem(i)) : zero;
       }
 #pragma unroll
       for (int i = 0; i < kL; ++i) {
         const bool fresh = i % G::kLoads == i_new && mine;
-        vr[i] = load_kv16(fresh ? nr.v + (i / G::kLoads) * D : v_head + off + elem(i));
+        const bool live = (i % G::kLoads) * G::kTokPerLoad + row < tail_valid;
+        vr[i] = live ? load_kv16(fresh ? nr.v + (i / G::kLoads) * D : v_head + off + elem(i)) : zero;
       }
       if (tail_valid == G::kUnitTok) {  // only with nr.on: the new token closes its unit,
         fold_whole(kr, vr);             // folded whole as without it

@@ -815,16 +815,42 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
   const int s0 = prm.group_starts[grp];
   const int n_seqs = prm.group_starts[grp + 1] - s0;
   if (qtile * kTile >= n_seqs) return;  // an empty group, or a tile past its members
-  const int plen = prm.prefix_lens[s0];
   const int P = prm.partition_tokens;
   const int tok_begin = part * P;
+  const int tile_begin = tok_begin / kTile;
+  const int* table = prm.block_tables + static_cast<size_t>(s0) * prm.max_blocks_per_seq;
+
+  // B operand of the score product for the queries q0 .. q0 + 15: query q0 + c16,
+  // dims [32c + 8j, +8) per step c
+  u32x4 qv[kQLoads];
+  auto load_queries = [&](int q0) {
+    if (q0 + c16 < n_seqs) {
+      const _Float16* qp = static_cast<const _Float16*>(prm.query) +
+                           (static_cast<size_t>(s0 + q0 + c16) * prm.num_heads + head) * D + 8 * j;
+#pragma unroll
+      for (int i = 0; i < kQLoads; ++i) qv[i] = load16(qp + 32 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kQLoads; ++i) qv[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // Issued before the prefix length is read, so that the K/V stream waits on one
+  // dependent load (the group's first sequence) instead of two: the first tile of
+  // queries, and the block ids of this wave's first 64 tiles, bounded by the partition
+  // and the table row rather than by the prefix (entries past it are read, never used).
+  load_queries(qtile * kTile);
+  const int first_tile = tile_begin + wave + lane * kPrefixWaves;
+  const int ids_first = wave + lane * kPrefixWaves < P / kTile &&
+                                first_tile < prm.max_blocks_per_seq * kTilesPerBlock
+                            ? table[first_tile / kTilesPerBlock]
+                            : 0;
+
+  const int plen = prm.prefix_lens[s0];
   if (tok_begin >= plen) return;
   const int tok_end = min(plen, tok_begin + P);  // plen is a whole number of tiles
-  const int tile_begin = tok_begin / kTile;
   const int n_tiles = (tok_end - tok_begin) / kTile;
   const int n_mine = n_tiles > wave ? (n_tiles - wave + kPrefixWaves - 1) / kPrefixWaves : 0;
 
-  const int* table = prm.block_tables + static_cast<size_t>(s0) * prm.max_blocks_per_seq;
   const size_t block_stride = static_cast<size_t>(prm.num_heads) * BS * D;  // elements
   const _Float16* k_head = static_cast<const _Float16*>(prm.key_cache) + static_cast<size_t>(head) * BS * D;
   const _Float16* v_head = static_cast<const _Float16*>(prm.value_cache) + static_cast<size_t>(head) * BS * D;
@@ -851,17 +877,7 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
   // Tiles qtile, qtile + query_tiles, ...: with query_tiles at least the group size
   // / 16 (the usual case) one tile, every tile of the group in a workgroup of its own.
   for (int q0 = qtile * kTile; q0 < n_seqs; q0 += prm.query_tiles * kTile) {
-    // B operand of the score product: query q0 + c16, dims [32c + 8j, +8) per step c
-    u32x4 qv[kQLoads];
-    if (q0 + c16 < n_seqs) {
-      const _Float16* qp = static_cast<const _Float16*>(prm.query) +
-                           (static_cast<size_t>(s0 + q0 + c16) * prm.num_heads + head) * D + 8 * j;
-#pragma unroll
-      for (int i = 0; i < kQLoads; ++i) qv[i] = load16(qp + 32 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kQLoads; ++i) qv[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    if (q0 != qtile * kTile) load_queries(q0);
 
     float m = -INFINITY;  // running max (base 2) of query c16
     float l = 0.0f;
@@ -933,9 +949,9 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
     for (int base = 0; base < n_mine; base += kWave) {
       // physical block of each of this wave's tiles, one per lane
       const int idx = base + lane;
-      const int ids = idx < n_mine
-                          ? table[(tile_begin + wave + idx * kPrefixWaves) / kTilesPerBlock]
-                          : 0;
+      const int ids = base == 0 ? ids_first
+                      : idx < n_mine ? table[(tile_begin + wave + idx * kPrefixWaves) / kTilesPerBlock]
+                                     : 0;
       const int n_here = min(n_mine - base, kWave);
       // the wave's i-th tile of this chunk: K as 16-byte runs of the row-major tile,
       // one contiguous KiB per load instruction (regrouped through LDS when folded),

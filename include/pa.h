@@ -40,8 +40,8 @@
  *                            A negative slot means "skip this row".
  *      block_pairs           int32 [num_pairs, 2] = (source block, destination block).
  *  * Supported shapes: head_dim in {64, 80, 96, 128, 256}; block_size in {8, 16,
- *    32, 64, 128, 256} (pa_decode_shared_prefix: fp16, head_dim 64 or 128,
- *    block_size 16 to 256); other values return PA_ERR_UNSUPPORTED.  K/V heads
+ *    32, 64, 128, 256} (pa_decode_shared_prefix: fp16, head_dim 64, 128 or 256,
+ *    block_size 8 to 256); other values return PA_ERR_UNSUPPORTED.  K/V heads
  *    equal query heads.
  *  * Errors: argument checks run on the host before anything is enqueued and return
  *    a status; nothing aborts and no C++ exception crosses the ABI.  A failed launch
@@ -397,20 +397,24 @@ pa_status pa_swap_blocks(void* dst_key, void* dst_value, const void* src_key,
  * Both are <= max_blocks_per_seq * block_size, and every context_lens[s] is too.
  * Groups of any size are accepted; a group's prefix is read once per 16 members, by
  * workgroups that run side by side.
- * Built for PA_F16, head_dim in {64, 128} and block_size in {16, 32, 64, 128, 256};
- * other values return PA_ERR_UNSUPPORTED.  partition_size applies to the tokens after the prefix
- * (as in pa_decode, sized by max_suffix_len); prefix_partition_size is the number
- * of prefix tokens one workgroup reads (0 = library choice, else a positive
- * multiple of max(16, block_size)).  The contents above are caller preconditions
- * (unchecked device data, as for pa_decode).
+ * Built for PA_F16, head_dim in {64, 128, 256} and block_size in {8, 16, 32, 64, 128,
+ * 256}; other values return PA_ERR_UNSUPPORTED.  The prefix pass reads whole tiles of 16
+ * tokens: with block_size 8, the prefix of a sequence whose prefix_lens[s] is an odd
+ * number of blocks is read by the pass after the prefix from its last 8 tokens on (the
+ * rounded length below is P0 = prefix_lens[s] rounded down to a multiple of 16; P0 =
+ * prefix_lens[s] for block_size >= 16).  partition_size applies to the tokens after P0
+ * (as in pa_decode, sized by max_suffix_len, plus 8 with block_size 8);
+ * prefix_partition_size is the number of prefix tokens one workgroup reads (0 = library
+ * choice, else a positive multiple of max(16, block_size)).  The contents above are
+ * caller preconditions (unchecked device data, as for pa_decode).
  *
  * Workspace (always needed when num_seqs > 0), float32, with NPp = prefix
  * partitions, NPs = partitions after the prefix and NS = NPp + NPs:
  *     m [num_seqs, num_heads, NS]   at byte 0
  *     l [num_seqs, num_heads, NS]   at byte ws_align(S*H*NS*4)
  *     o [num_seqs, num_heads, NS, head_dim]   at byte 2*ws_align(S*H*NS*4)
- * Slot p < NPp holds the state of prefix tokens [p*Pp, (p+1)*Pp) and slot NPp + p
- * that of tokens [prefix_lens[s] + p*P, prefix_lens[s] + (p+1)*P), with the same
+ * Slot p < NPp holds the state of prefix tokens [p*Pp, min((p+1)*Pp, P0)) and slot
+ * NPp + p that of tokens [P0 + p*P, P0 + (p+1)*P), with the same
  * (m, l, o) definition as pa_decode's workspace.  Slots past a sequence's tokens are
  * not written, nor are the slots after the prefix of a sequence whose remaining
  * tokens fit one partition: that partition's workgroup merges the prefix states and

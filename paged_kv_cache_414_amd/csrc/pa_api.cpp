@@ -328,10 +328,11 @@ pa_status plan_shared(SharedPlan* plan, int32_t num_seqs, int32_t num_heads, int
                       int32_t block_size, int32_t num_groups, int32_t max_group_size,
                       int32_t max_prefix_len, int32_t max_suffix_len, int32_t partition_size,
                       int32_t prefix_partition_size) {
-  if (head_dim != 64 && head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 128)", head_dim);
-  if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128 && block_size != 256)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not built for the shared-prefix decode (16 to 256)",
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 128, 256)", head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128 &&
+      block_size != 256)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not built for the shared-prefix decode (8 to 256)",
                 block_size);
   if (num_seqs < 0 || num_heads <= 0 || num_groups < 0)
     return fail(PA_ERR_INVALID_ARG, "num_seqs %d >= 0, num_heads %d > 0, num_groups %d >= 0 required",
@@ -347,13 +348,16 @@ pa_status plan_shared(SharedPlan* plan, int32_t num_seqs, int32_t num_heads, int
   const int32_t Pp = resolve_prefix_partition(num_groups, QT, num_heads, block_size, max_prefix_len,
                                               prefix_partition_size);
   if (Pp < 0) return PA_ERR_INVALID_ARG;
-  const int32_t P = resolve_partition(num_seqs, num_heads, block_size, max_suffix_len, partition_size);
+  // The prefix pass reads whole 16-token tiles: with blocks of 8 tokens a prefix may end
+  // half a tile past the last whole tile, and those 8 tokens join the pass after it.
+  const int32_t suffix_cap = max_suffix_len + (block_size < kPrefixTile ? kPrefixTile - block_size : 0);
+  const int32_t P = resolve_partition(num_seqs, num_heads, block_size, suffix_cap, partition_size);
   if (P < 0) return PA_ERR_INVALID_ARG;
   plan->Pp = Pp;
   plan->QT = QT;
   plan->NPp = max_prefix_len > 0 ? partitions_for(max_prefix_len, Pp) : 0;
   plan->P = P;
-  plan->NPs = partitions_for(max_suffix_len, P);
+  plan->NPs = partitions_for(suffix_cap, P);
   plan->slots = plan->NPp + plan->NPs;
   const size_t states = static_cast<size_t>(num_seqs) * num_heads * plan->slots;
   plan->ws_bytes = num_seqs > 0 ? 2 * ws_align(states * 4) + ws_align(states * head_dim * 4) : 0;

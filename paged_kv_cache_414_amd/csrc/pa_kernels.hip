@@ -65,6 +65,14 @@ constexpr int kWavesNarrow = kDecodeWavesNarrow;  // the two decode workgroup si
 constexpr int kWavesWide = kDecodeWavesWide;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Tokens (and queries) per matrix-core tile of the shared-prefix decode.  The prefix
+// pass reads a sequence's shared prefix in whole tiles: with blocks of 8 tokens a prefix
+// that ends inside a tile is rounded down to whole tiles, and the pass after the prefix
+// starts at that rounded length (with blocks of 16 tokens or more every prefix is a whole
+// number of tiles already).  Every reader of the prefix lengths applies tiled_prefix.
+constexpr int kTile = 16;
+__device__ __forceinline__ int tiled_prefix(int prefix_len) { return prefix_len & ~(kTile - 1); }
+
 // ---------------------------------------------------------------------------------
 // small device helpers
 // ---------------------------------------------------------------------------------
@@ -544,7 +552,7 @@ __device__ __forceinline__ void partitions_workgroup(const DecodeParams& prm, in
   // grid slice z decodes sequence z, or seq_order[z] when the caller ordered the launch
   const int seq = prm.seq_order ? __builtin_amdgcn_readfirstlane(prm.seq_order[z]) : z;
   const int P = prm.partition_tokens;
-  const int start = prm.token_begin ? prm.token_begin[seq] : 0;  // a multiple of BS
+  const int start = prm.token_begin ? tiled_prefix(prm.token_begin[seq]) : 0;  // a multiple of BS
   const int tok_begin = start + part * P;
   const int unit_begin = tok_begin / G::kUnitTok;  // P and start are multiples of BS
 
@@ -701,7 +709,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(ReduceParams prm) {
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
   const int ctx = prm.context_lens[seq];
-  const int start = prm.prefix_lens ? prm.prefix_lens[seq] : 0;
+  const int start = prm.prefix_lens ? tiled_prefix(prm.prefix_lens[seq]) : 0;
   const int P = prm.partition_tokens;
   const int Pp = prm.prefix_partition_tokens;
   const int np_suffix = ctx > start ? (ctx - start + P - 1) / P : 0;
@@ -778,7 +786,6 @@ constexpr int kPrefixWaves = PA_PREFIX_WAVES;
 constexpr int kPrefixSlots = kPrefixWaves > 4 ? kPrefixWaves / 2 : kPrefixWaves;
 constexpr int kPrefixThreads = kPrefixWaves * kWave;
 static_assert(kPrefixWaves == kPrefixSlots || kPrefixWaves == 2 * kPrefixSlots, "prefix waves");
-constexpr int kTile = 16;  // tokens and queries per matrix-core tile
 
 // One lane's run of kN fp16 values of a V row (kN = 8: 16 bytes, kN = 4: 8 bytes).
 template <int kN> struct HalfRun;
@@ -786,6 +793,14 @@ template <> struct HalfRun<8> {
   u32x4 w;
   __device__ __forceinline__ void load(const _Float16* p) { w = load_kv16(p); }
   __device__ __forceinline__ _Float16 at(int i) const { return as_h2(w[i / 2])[i % 2]; }
+};
+template <> struct HalfRun<16> {
+  u32x4 w[2];
+  __device__ __forceinline__ void load(const _Float16* p) {
+    w[0] = load_kv16(p);
+    w[1] = load_kv16(p + 8);
+  }
+  __device__ __forceinline__ _Float16 at(int i) const { return as_h2(w[i / 8][(i % 8) / 2])[i % 2]; }
 };
 template <> struct HalfRun<4> {
   u32x2 w;
@@ -797,8 +812,12 @@ template <> struct HalfRun<4> {
 
 template <int D, int BS>
 __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int part, int head, int zz) {
-  static_assert(BS % kTile == 0 && (D == 64 || D == 128), "shape");
-  constexpr int kTilesPerBlock = BS / kTile;
+  static_assert((BS % kTile == 0 || BS == kTile / 2) && (D == 64 || D == 128 || D == 256), "shape");
+  // a tile lies in one block (kTilesPerBlock tiles per block), or with blocks of 8 tokens
+  // spans two (its first 8 token rows in block 2t of the table, the last 8 in block 2t + 1)
+  constexpr int kBlocksPerTile = BS < kTile ? kTile / BS : 1;
+  constexpr int kTilesPerBlock = BS < kTile ? 1 : BS / kTile;
+  auto table_index = [](int tile, int k) { return kBlocksPerTile == 1 ? tile / kTilesPerBlock : 2 * tile + k; };
   // score product: step c (of kQLoads) gives lane group j the dims
   // [32c + 8j, 32c + 8j + 8) of its K row and query -- one 16-byte load each, and the
   // four lane groups of a row read 64 contiguous bytes per load instruction
@@ -840,14 +859,16 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
   // and the table row rather than by the prefix (entries past it are read, never used).
   load_queries(qtile * kTile);
   const int first_tile = tile_begin + wave + lane * kPrefixWaves;
-  const int ids_first = wave + lane * kPrefixWaves < P / kTile &&
-                                first_tile < prm.max_blocks_per_seq * kTilesPerBlock
-                            ? table[first_tile / kTilesPerBlock]
-                            : 0;
+  int ids_first[kBlocksPerTile];
+#pragma unroll
+  for (int k = 0; k < kBlocksPerTile; ++k)
+    ids_first[k] = wave + lane * kPrefixWaves < P / kTile && table_index(first_tile, k) < prm.max_blocks_per_seq
+                       ? table[table_index(first_tile, k)]
+                       : 0;
 
-  const int plen = prm.prefix_lens[s0];
+  const int plen = tiled_prefix(prm.prefix_lens[s0]);
   if (tok_begin >= plen) return;
-  const int tok_end = min(plen, tok_begin + P);  // plen is a whole number of tiles
+  const int tok_end = min(plen, tok_begin + P);  // a whole number of tiles
   const int n_tiles = (tok_end - tok_begin) / kTile;
   const int n_mine = n_tiles > wave ? (n_tiles - wave + kPrefixWaves - 1) / kPrefixWaves : 0;
 
@@ -947,24 +968,43 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
     };
 
     for (int base = 0; base < n_mine; base += kWave) {
-      // physical block of each of this wave's tiles, one per lane
+      // physical block(s) of each of this wave's tiles, one tile per lane
       const int idx = base + lane;
-      const int ids = base == 0 ? ids_first
-                      : idx < n_mine ? table[(tile_begin + wave + idx * kPrefixWaves) / kTilesPerBlock]
-                                     : 0;
+      int ids[kBlocksPerTile];
+#pragma unroll
+      for (int k = 0; k < kBlocksPerTile; ++k)
+        ids[k] = base == 0      ? ids_first[k]
+                 : idx < n_mine ? table[table_index(tile_begin + wave + idx * kPrefixWaves, k)]
+                                : 0;
       const int n_here = min(n_mine - base, kWave);
       // the wave's i-th tile of this chunk: K as 16-byte runs of the row-major tile,
       // one contiguous KiB per load instruction (regrouped through LDS when folded),
       // and V rows 4j+v (dims [kDv*c16, +kDv))
       auto load_tile = [&](int i, u32x4 (&kv)[kQLoads], HalfRun<kDv> (&vr)[4]) {
         const int tile = tile_begin + wave + (base + i) * kPrefixWaves;
-        const int phys = __builtin_amdgcn_readlane(ids, i);
-        const size_t off = static_cast<size_t>(phys) * block_stride +
-                           static_cast<size_t>(tile % kTilesPerBlock) * kTile * D;
+        if constexpr (kBlocksPerTile == 1) {
+          const int phys = __builtin_amdgcn_readlane(ids[0], i);
+          const size_t off = static_cast<size_t>(phys) * block_stride +
+                             static_cast<size_t>(tile % kTilesPerBlock) * kTile * D;
 #pragma unroll
-        for (int ii = 0; ii < kQLoads; ++ii) kv[ii] = load_kv16(k_head + off + 512 * ii + 8 * lane);
+          for (int ii = 0; ii < kQLoads; ++ii) kv[ii] = load_kv16(k_head + off + 512 * ii + 8 * lane);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) vr[v].load(v_head + off + (4 * j + v) * D + kDv * c16);
+          for (int v = 0; v < 4; ++v) vr[v].load(v_head + off + (4 * j + v) * D + kDv * c16);
+        } else {
+          // token rows 0-7 from the first block, 8-15 from the second: K loads
+          // 0 .. kQLoads / 2 - 1 cover the first 8 rows (each load 512 / D rows)
+          const size_t off0 = static_cast<size_t>(__builtin_amdgcn_readlane(ids[0], i)) * block_stride;
+          const size_t off1 = static_cast<size_t>(__builtin_amdgcn_readlane(ids[1], i)) * block_stride;
+#pragma unroll
+          for (int ii = 0; ii < kQLoads; ++ii) {
+            constexpr int kHalf = kQLoads / 2;
+            kv[ii] = ii < kHalf ? load_kv16(k_head + off0 + 512 * ii + 8 * lane)
+                                : load_kv16(k_head + off1 + 512 * (ii - kHalf) + 8 * lane);
+          }
+          const size_t off_v = j < 2 ? off0 : off1;  // rows 4j .. 4j + 3
+#pragma unroll
+          for (int v = 0; v < 4; ++v) vr[v].load(v_head + off_v + (4 * (j % 2) + v) * D + kDv * c16);
+        }
       };
 #if PA_PREFIX_PREFETCH
       // two tiles in registers: the next tile's loads are in flight while the
@@ -1223,6 +1263,9 @@ template <int D>
 static hipError_t launch_prefix_d(const PrefixParams& prm, int block_size, hipStream_t stream) {
   dim3 grid(prm.num_partitions, prm.num_heads, prm.num_groups * prm.query_tiles);
   switch (block_size) {
+    case 8:
+      hipLaunchKernelGGL((decode_prefix_kernel<D, 8>), grid, dim3(kPrefixThreads), 0, stream, prm);
+      break;
     case 16:
       hipLaunchKernelGGL((decode_prefix_kernel<D, 16>), grid, dim3(kPrefixThreads), 0, stream, prm);
       break;
@@ -1254,6 +1297,7 @@ static hipError_t launch_fused_d(const PrefixParams& pp, const DecodeParams& dp,
   const dim3 grid(static_cast<unsigned>(groups));
   const int32_t pg = static_cast<int32_t>(prefix_groups);
   switch (block_size) {
+    case 8: hipLaunchKernelGGL((decode_shared_fused_kernel<D, 8>), grid, dim3(kPrefixThreads), 0, stream, pp, dp, pg); break;
     case 16: hipLaunchKernelGGL((decode_shared_fused_kernel<D, 16>), grid, dim3(kPrefixThreads), 0, stream, pp, dp, pg); break;
     case 32: hipLaunchKernelGGL((decode_shared_fused_kernel<D, 32>), grid, dim3(kPrefixThreads), 0, stream, pp, dp, pg); break;
     case 64: hipLaunchKernelGGL((decode_shared_fused_kernel<D, 64>), grid, dim3(kPrefixThreads), 0, stream, pp, dp, pg); break;
@@ -1269,6 +1313,7 @@ hipError_t launch_decode_shared_fused(const PrefixParams& pp, const DecodeParams
   switch (head_dim) {
     case 64: return launch_fused_d<64>(pp, dp, block_size, stream);
     case 128: return launch_fused_d<128>(pp, dp, block_size, stream);
+    case 256: return launch_fused_d<256>(pp, dp, block_size, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1279,6 +1324,7 @@ hipError_t launch_decode_prefix(const PrefixParams& prm, int head_dim, int block
   switch (head_dim) {
     case 64: return launch_prefix_d<64>(prm, block_size, stream);
     case 128: return launch_prefix_d<128>(prm, block_size, stream);
+    case 256: return launch_prefix_d<256>(prm, block_size, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -181,7 +181,7 @@ def _bad_shared(ops, **over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(dtype=0), 3),            # fp32 is not built for the shared-prefix decode
-    (dict(bs=8), 3),
+    (dict(bs=4), 3),
     (dict(D=96), 3),
     (dict(maxp=40), 2),            # not a whole number of blocks
     (dict(maxp=-16), 2),
@@ -244,6 +244,20 @@ def test_shared_prefix_planning(ops):
     assert prefix_slots(1, 0, 1024) == 2        # 0: the average group (64 members) decides
     assert prefix_slots(2, 0, 1024) == 2        # average 32 members: 2 x 2 x 32 = 128
     assert prefix_slots(1, 128, 512) == 1       # 8 tiles x 32 = 256 already
+    # head dims 64, 128 and 256 are built for the shared-prefix decode; others are refused
+    for dd in (64, 256):
+        assert ops.pa_decode_shared_prefix_workspace_bytes(s, h, dd, 16, 8, 1024, 272) > 0
+    for dd in (80, 96):
+        assert ops.lib.pa_decode_shared_prefix_workspace_bytes(s, h, dd, 16, 8, 0, 1024, 272, 0, 0) == 0
+        assert b"head_dim" in ops.lib.pa_last_error()
+    # blocks of 8 tokens: the pass after the prefix is planned for 8 more tokens (a prefix
+    # may end half a 16-token tile past the prefix pass's last whole tile)
+    n8 = ops.pa_decode_shared_prefix_workspace_bytes(s, h, d, 8, 8, 1024, 256, 256, 256)
+    slots8 = 4 + ops.pa_decode_num_partitions(s, h, 8, 264, 256)
+    assert slots8 == 6
+    ml8 = -(-(s * h * slots8 * 4) // 256) * 256
+    assert n8 == 2 * ml8 + s * h * slots8 * d * 4
+    assert ops.lib.pa_decode_shared_prefix_workspace_bytes(s, h, d, 4, 8, 0, 1024, 272, 0, 0) == 0
     # a prefix that is not a whole number of blocks is refused
     assert ops.lib.pa_decode_shared_prefix_workspace_bytes(s, h, d, 16, 8, 0, 1000, 272, 0, 0) == 0
     assert ops.lib.pa_last_error() != b""

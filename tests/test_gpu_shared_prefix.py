@@ -70,6 +70,11 @@ CASES = [
     ("no_groups", 128, 16, [], (0, 0), (1, 200), 5, 0, 0),
     ("bs64", 128, 64, [8, 3], (1, 5), (1, 150), 1, 0, 0),
     ("bs256", 64, 256, [6], (1, 2), (1, 300), 0, 0, 256),
+    ("d256", 256, 16, [8, 5, 17], (1, 6), (0, 60), 1, 0, 0),
+    ("d256_bs64", 256, 64, [3, 12], (1, 3), (1, 100), 0, 128, 64),
+    ("bs8", 128, 8, [8, 7, 1], (1, 9), (0, 50), 2, 0, 0),
+    ("bs8_d64_parts", 64, 8, [4, 20], (3, 40), (1, 120), 1, 40, 48),
+    ("bs8_d256", 256, 8, [6, 6], (2, 5), (0, 30), 0, 0, 16),
 ]
 
 
@@ -108,17 +113,24 @@ def test_prefix_partition_sizes_agree():
         assert max_abs_err(run_shared(b, 0, pp), want) <= TOL, pp
 
 
-def test_prefix_states_match_oracle():
+@pytest.mark.parametrize("head_dim,block_size", [(64, 16), (256, 16), (128, 8)])
+def test_prefix_states_match_oracle(head_dim, block_size):
     """Prefix slots of the workspace (base-2 m, l, o) against the oracle's partition
-    states over the same prefix token ranges: m2 = m * log2(e)."""
+    states over the same prefix token ranges: m2 = m * log2(e).  The prefix pass reads
+    whole 16-token tiles, so with blocks of 8 tokens the states cover each prefix
+    rounded down to a multiple of 16 (the rest joins the pass after the prefix, whose
+    partitions are planned for up to 8 more tokens)."""
     from paged_kv_cache_414_amd import ops
     b = workloads.make_shared_prefix_batch("pstates", seed=41, group_sizes=[5, 3], num_heads=2,
-                                           head_dim=64, block_size=16, prefix_blocks_low=6,
-                                           prefix_blocks_high=9, suffix_low=1, suffix_high=30)
+                                           head_dim=head_dim, block_size=block_size,
+                                           prefix_blocks_low=6 * 16 // block_size,
+                                           prefix_blocks_high=9 * 16 // block_size + 1,
+                                           suffix_low=1, suffix_high=30)
     Pp, P = 32, 64
     _, ws = run_shared(b, P, Pp, return_ws=True)
     n_prefix = -(-b.max_prefix_len // Pp)
-    slots = n_prefix + ops.pa_decode_num_partitions(b.num_seqs, 2, 16, b.max_suffix_len, P)
+    suffix_cap = b.max_suffix_len + (16 - block_size if block_size < 16 else 0)
+    slots = n_prefix + ops.pa_decode_num_partitions(b.num_seqs, 2, block_size, suffix_cap, P)
     s_count, h_count, d = b.q.shape
     n = s_count * h_count * slots
     ml = -(-(n * 4) // 256) * 256
@@ -129,7 +141,7 @@ def test_prefix_states_match_oracle():
     log2e = 1.0 / np.log(2.0)
     checked = 0
     for s in range(s_count):
-        plen = int(b.prefix_lens[s])
+        plen = int(b.prefix_lens[s]) // 16 * 16
         for h in range(h_count):
             for p in range(-(-plen // Pp)):
                 mo, lo, oo = oracle.partition_state(b.q[s, h], b.k_pool, b.v_pool,
@@ -237,6 +249,39 @@ def test_random_shared_prefix_layouts(i):
     b = workloads.make_shared_prefix_batch(f"random{i}", seed=3000 + i, group_sizes=sizes,
                                            num_heads=2, head_dim=d, block_size=bs,
                                            prefix_blocks_low=plo, prefix_blocks_high=phi,
+                                           suffix_low=slo, suffix_high=shi, ungrouped=ungrouped,
+                                           pool_slack=1.3)
+    got = run_shared(b, part, ppart, max_group_size=mgs)
+    assert np.all(np.isfinite(got)), i
+    assert max_abs_err(got, _oracle(b)) <= TOL, i
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shared_prefix_layouts_head_dim_256(i):
+    """The same random layouts at head dim 256 (the prefix pass's widest tiles: 8 score
+    steps and 16 value tiles per wave)."""
+    _, bs, sizes, (plo, phi), (slo, shi), ungrouped, part, ppart, mgs = _draw_shared_case(100 + i)
+    b = workloads.make_shared_prefix_batch(f"random256_{i}", seed=4000 + i, group_sizes=sizes,
+                                           num_heads=2, head_dim=256, block_size=bs,
+                                           prefix_blocks_low=plo, prefix_blocks_high=phi,
+                                           suffix_low=slo, suffix_high=shi, ungrouped=ungrouped,
+                                           pool_slack=1.3)
+    got = run_shared(b, part, ppart, max_group_size=mgs)
+    assert np.all(np.isfinite(got)), i
+    assert max_abs_err(got, _oracle(b)) <= TOL, i
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shared_prefix_layouts_block_size_8(i):
+    """Random layouts with blocks of 8 tokens: a 16-token tile spans two blocks, and a
+    prefix of an odd number of blocks ends half a tile past the last whole tile."""
+    rng = np.random.default_rng([2027, i])
+    d, _, sizes, (plo, phi), (slo, shi), ungrouped, _, _, mgs = _draw_shared_case(200 + i)
+    part = 0 if rng.random() < 0.5 else 8 * int(rng.integers(1, 65))
+    ppart = 0 if rng.random() < 0.5 else 16 * int(rng.integers(1, 33))
+    b = workloads.make_shared_prefix_batch(f"random_bs8_{i}", seed=5000 + i, group_sizes=sizes,
+                                           num_heads=2, head_dim=d, block_size=8,
+                                           prefix_blocks_low=plo, prefix_blocks_high=2 * phi + 1,
                                            suffix_low=slo, suffix_high=shi, ungrouped=ungrouped,
                                            pool_slack=1.3)
     got = run_shared(b, part, ppart, max_group_size=mgs)

@@ -248,6 +248,28 @@ def test_groups_with_empty_and_single_members_and_decode_again():
     _pools_equal(kc, vc, host)
 
 
+def test_groups_with_blocks_of_8_tokens():
+    """Grouped steps with blocks of 8 tokens: the members share 9 whole blocks (72
+    tokens), half a 16-token tile past the prefix pass's last whole tile, so those 8
+    tokens are read by the pass after the prefix."""
+    bm, kc, vc, eng, host = _setup(nb=300, h=4, bs=8, d=128, seed=9, max_seqs=8, mb=24,
+                                   admit=0, groups=2)
+    rng = np.random.default_rng(7)
+    _seed_sequence(bm, kc, vc, host, rng, 0, 75)
+    for child in (1, 2, 3, 4):
+        bm.fork(0, child)
+    _seed_sequence(bm, kc, vc, host, rng, 5, 40)
+    starts = np.array([0, 5, 6], dtype=np.int32)  # {0, .., 4}, {5}
+    ids = [0, 1, 2, 3, 4, 5]
+    for step in range(4):
+        note(f"grouped step {step}, blocks of 8 tokens")
+        res, view, out, q = _step(eng, host, rng, ids, 0.09, group_starts=starts)
+        assert view["prefix_lens"][:5].tolist() == [72] * 5
+        if step == 0:
+            assert res.num_copies == 4  # 75 % 8 != 0: four of the five sharers copy
+    _pools_equal(kc, vc, host)
+
+
 def test_one_launch_steps_and_decode_again():
     """Steps with no copy-on-write and no groups are one decode launch that reads the
     staged arrays from the pinned buffer; the view exposes that buffer, and the decode

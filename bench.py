@@ -580,20 +580,24 @@ def append_copy_throughput(torch, ops, metrics, args):
 
 
 def shared_prefix_groups(torch, ops, metrics, args):
-    """pa_decode against pa_decode_shared_prefix for other group layouts (32 heads x
-    128, block 16, fp16; each member holds 200-330 tokens of its own after the shared
-    prefix): many small groups, one group of 64 sharing a long prompt, and one group of
-    256 (a prompt shared by the whole batch)."""
+    """pa_decode against pa_decode_shared_prefix for other group layouts (32 heads, fp16;
+    each member holds 200-330 tokens of its own after the shared prefix): many small
+    groups, one group of 64 sharing a long prompt and one group of 256 (a prompt shared
+    by the whole batch), at head dim 128 and block 16; and the small groups at head dim
+    256, and with blocks of 8 tokens and a prefix of an odd number of blocks."""
     from paged_kv_cache_414_amd import workloads
 
     log(args, "shared-prefix group layouts")
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     rows = []
-    for sizes, prefix_blocks in (([8] * 8, 64), ([64], 128), ([256], 32)):
+    # (group sizes, shared tokens, head dim, block size)
+    for sizes, prefix_tokens, hd, bs in (([8] * 8, 1024, 128, 16), ([64], 2048, 128, 16),
+                                         ([256], 512, 128, 16), ([8] * 8, 1024, 256, 16),
+                                         ([8] * 8, 1032, 128, 8)):
         b = workloads.make_shared_prefix_batch("groups", seed=3, group_sizes=sizes, num_heads=32,
-                                               head_dim=128, block_size=16,
-                                               prefix_blocks_low=prefix_blocks,
-                                               prefix_blocks_high=prefix_blocks, suffix_low=200,
+                                               head_dim=hd, block_size=bs,
+                                               prefix_blocks_low=prefix_tokens // bs,
+                                               prefix_blocks_high=prefix_tokens // bs, suffix_low=200,
                                                suffix_high=330, poison=False)
         q, k, v = dev(b.q), dev(b.k_pool), dev(b.v_pool)
         tables, ctx = dev(b.block_tables), dev(b.context_lens)
@@ -620,7 +624,8 @@ def shared_prefix_groups(torch, ops, metrics, args):
         per_token = metrics.kv_bytes_per_token(1, b.num_heads, b.head_dim, 2)
         unique = per_token * int((b.context_lens - b.prefix_lens).sum() +
                                  b.prefix_lens[b.group_starts[:-1]].sum())
-        rows.append({"groups": f"{len(sizes)} x {sizes[0]}", "prefix_tokens": prefix_blocks * 16,
+        rows.append({"groups": f"{len(sizes)} x {sizes[0]}", "prefix_tokens": prefix_tokens,
+                     "head_dim": hd, "block_size": bs,
                      "pa_decode_ms": round(ms_plain, 5),
                      "pa_decode_shared_prefix_ms": round(ms_shared, 5),
                      "speedup": round(ms_plain / ms_shared, 3),

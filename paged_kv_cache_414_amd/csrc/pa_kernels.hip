@@ -787,7 +787,7 @@ constexpr int kPrefixSlots = kPrefixWaves > 4 ? kPrefixWaves / 2 : kPrefixWaves;
 constexpr int kPrefixThreads = kPrefixWaves * kWave;
 static_assert(kPrefixWaves == kPrefixSlots || kPrefixWaves == 2 * kPrefixSlots, "prefix waves");
 
-// One lane's run of kN fp16 values of a V row (kN = 8: 16 bytes, kN = 4: 8 bytes).
+// One lane's run of kN fp16 values of a V row (kN = D / 16: 8, 12, 16 or 32 bytes).
 template <int kN> struct HalfRun;
 template <> struct HalfRun<8> {
   u32x4 w;
@@ -802,6 +802,16 @@ template <> struct HalfRun<16> {
   }
   __device__ __forceinline__ _Float16 at(int i) const { return as_h2(w[i / 8][(i % 8) / 2])[i % 2]; }
 };
+template <> struct HalfRun<6> {
+  uint32_t w[3];
+  __device__ __forceinline__ void load(const _Float16* p) {
+    const uint32_t* u = reinterpret_cast<const uint32_t*>(p);  // 4-byte aligned: 12 bytes per lane
+    w[0] = __builtin_nontemporal_load(u);
+    w[1] = __builtin_nontemporal_load(u + 1);
+    w[2] = __builtin_nontemporal_load(u + 2);
+  }
+  __device__ __forceinline__ _Float16 at(int i) const { return as_h2(w[i / 2])[i % 2]; }
+};
 template <> struct HalfRun<4> {
   u32x2 w;
   __device__ __forceinline__ void load(const _Float16* p) {
@@ -812,7 +822,7 @@ template <> struct HalfRun<4> {
 
 template <int D, int BS>
 __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int part, int head, int zz) {
-  static_assert((BS % kTile == 0 || BS == kTile / 2) && (D == 64 || D == 128 || D == 256), "shape");
+  static_assert((BS % kTile == 0 || BS == kTile / 2) && (D == 64 || D == 96 || D == 128 || D == 256), "shape");
   // a tile lies in one block (kTilesPerBlock tiles per block), or with blocks of 8 tokens
   // spans two (its first 8 token rows in block 2t of the table, the last 8 in block 2t + 1)
   constexpr int kBlocksPerTile = BS < kTile ? kTile / BS : 1;
@@ -991,15 +1001,15 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
 #pragma unroll
           for (int v = 0; v < 4; ++v) vr[v].load(v_head + off + (4 * j + v) * D + kDv * c16);
         } else {
-          // token rows 0-7 from the first block, 8-15 from the second: K loads
-          // 0 .. kQLoads / 2 - 1 cover the first 8 rows (each load 512 / D rows)
+          // token rows 0-7 from the first block, 8-15 from the second: element e of
+          // the row-major tile lies in the second block from e = 8 * D on (a load may
+          // straddle that boundary between lanes, never within a lane's 8 elements)
           const size_t off0 = static_cast<size_t>(__builtin_amdgcn_readlane(ids[0], i)) * block_stride;
           const size_t off1 = static_cast<size_t>(__builtin_amdgcn_readlane(ids[1], i)) * block_stride;
 #pragma unroll
           for (int ii = 0; ii < kQLoads; ++ii) {
-            constexpr int kHalf = kQLoads / 2;
-            kv[ii] = ii < kHalf ? load_kv16(k_head + off0 + 512 * ii + 8 * lane)
-                                : load_kv16(k_head + off1 + 512 * (ii - kHalf) + 8 * lane);
+            const int e = 512 * ii + 8 * lane;
+            kv[ii] = e < 8 * D ? load_kv16(k_head + off0 + e) : load_kv16(k_head + off1 + (e - 8 * D));
           }
           const size_t off_v = j < 2 ? off0 : off1;  // rows 4j .. 4j + 3
 #pragma unroll
@@ -1312,6 +1322,7 @@ hipError_t launch_decode_shared_fused(const PrefixParams& pp, const DecodeParams
                                       hipStream_t stream) {
   switch (head_dim) {
     case 64: return launch_fused_d<64>(pp, dp, block_size, stream);
+    case 96: return launch_fused_d<96>(pp, dp, block_size, stream);
     case 128: return launch_fused_d<128>(pp, dp, block_size, stream);
     case 256: return launch_fused_d<256>(pp, dp, block_size, stream);
     default: return hipErrorInvalidValue;
@@ -1323,6 +1334,7 @@ hipError_t launch_decode_prefix(const PrefixParams& prm, int head_dim, int block
                                 hipStream_t stream) {
   switch (head_dim) {
     case 64: return launch_prefix_d<64>(prm, block_size, stream);
+    case 96: return launch_prefix_d<96>(prm, block_size, stream);
     case 128: return launch_prefix_d<128>(prm, block_size, stream);
     case 256: return launch_prefix_d<256>(prm, block_size, stream);
     default: return hipErrorInvalidValue;

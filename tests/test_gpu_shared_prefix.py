@@ -75,6 +75,8 @@ CASES = [
     ("bs8", 128, 8, [8, 7, 1], (1, 9), (0, 50), 2, 0, 0),
     ("bs8_d64_parts", 64, 8, [4, 20], (3, 40), (1, 120), 1, 40, 48),
     ("bs8_d256", 256, 8, [6, 6], (2, 5), (0, 30), 0, 0, 16),
+    ("d96", 96, 16, [8, 3, 20], (1, 5), (0, 80), 1, 0, 0),
+    ("d96_bs8", 96, 8, [5, 9], (3, 13), (1, 60), 0, 0, 32),
 ]
 
 
@@ -113,7 +115,7 @@ def test_prefix_partition_sizes_agree():
         assert max_abs_err(run_shared(b, 0, pp), want) <= TOL, pp
 
 
-@pytest.mark.parametrize("head_dim,block_size", [(64, 16), (256, 16), (128, 8)])
+@pytest.mark.parametrize("head_dim,block_size", [(64, 16), (256, 16), (128, 8), (96, 8)])
 def test_prefix_states_match_oracle(head_dim, block_size):
     """Prefix slots of the workspace (base-2 m, l, o) against the oracle's partition
     states over the same prefix token ranges: m2 = m * log2(e).  The prefix pass reads
@@ -282,6 +284,23 @@ def test_random_shared_prefix_layouts_block_size_8(i):
     b = workloads.make_shared_prefix_batch(f"random_bs8_{i}", seed=5000 + i, group_sizes=sizes,
                                            num_heads=2, head_dim=d, block_size=8,
                                            prefix_blocks_low=plo, prefix_blocks_high=2 * phi + 1,
+                                           suffix_low=slo, suffix_high=shi, ungrouped=ungrouped,
+                                           pool_slack=1.3)
+    got = run_shared(b, part, ppart, max_group_size=mgs)
+    assert np.all(np.isfinite(got)), i
+    assert max_abs_err(got, _oracle(b)) <= TOL, i
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_shared_prefix_layouts_head_dim_96(i):
+    """Random layouts at head dim 96 (3 score steps and 6 value tiles per wave, V runs of
+    12 bytes per lane), block sizes 8 to 256."""
+    _, bs, sizes, (plo, phi), (slo, shi), ungrouped, part, ppart, mgs = _draw_shared_case(300 + i)
+    if i % 2:  # every other case with blocks of 8 tokens
+        bs, part = 8, 0
+    b = workloads.make_shared_prefix_batch(f"random96_{i}", seed=6000 + i, group_sizes=sizes,
+                                           num_heads=2, head_dim=96, block_size=bs,
+                                           prefix_blocks_low=plo, prefix_blocks_high=phi,
                                            suffix_low=slo, suffix_high=shi, ungrouped=ungrouped,
                                            pool_slack=1.3)
     got = run_shared(b, part, ppart, max_group_size=mgs)

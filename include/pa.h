@@ -40,7 +40,7 @@
  *                            A negative slot means "skip this row".
  *      block_pairs           int32 [num_pairs, 2] = (source block, destination block).
  *  * Supported shapes: head_dim in {64, 80, 96, 128, 256}; block_size in {8, 16,
- *    32, 64, 128, 256} (pa_decode_shared_prefix: fp16, head_dim 64, 96, 128 or 256,
+ *    32, 64, 128, 256} (pa_decode_shared_prefix: fp16, every head_dim above,
  *    block_size 8 to 256); other values return PA_ERR_UNSUPPORTED.  K/V heads
  *    equal query heads.
  *  * Errors: argument checks run on the host before anything is enqueued and return
@@ -397,7 +397,7 @@ pa_status pa_swap_blocks(void* dst_key, void* dst_value, const void* src_key,
  * Both are <= max_blocks_per_seq * block_size, and every context_lens[s] is too.
  * Groups of any size are accepted; a group's prefix is read once per 16 members, by
  * workgroups that run side by side.
- * Built for PA_F16, head_dim in {64, 96, 128, 256} and block_size in {8, 16, 32, 64, 128,
+ * Built for PA_F16, head_dim in {64, 80, 96, 128, 256} and block_size in {8, 16, 32, 64, 128,
  * 256}; other values return PA_ERR_UNSUPPORTED.  The prefix pass reads whole tiles of 16
  * tokens: with block_size 8, the prefix of a sequence whose prefix_lens[s] is an odd
  * number of blocks is read by the pass after the prefix from its last 8 tokens on (the

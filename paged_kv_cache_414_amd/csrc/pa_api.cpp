@@ -328,8 +328,8 @@ pa_status plan_shared(SharedPlan* plan, int32_t num_seqs, int32_t num_heads, int
                       int32_t block_size, int32_t num_groups, int32_t max_group_size,
                       int32_t max_prefix_len, int32_t max_suffix_len, int32_t partition_size,
                       int32_t prefix_partition_size) {
-  if (head_dim != 64 && head_dim != 96 && head_dim != 128 && head_dim != 256)
-    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 96, 128, 256)", head_dim);
+  if (head_dim != 64 && head_dim != 80 && head_dim != 96 && head_dim != 128 && head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not built (64, 80, 96, 128, 256)", head_dim);
   if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128 &&
       block_size != 256)
     return fail(PA_ERR_UNSUPPORTED, "block_size %d is not built for the shared-prefix decode (8 to 256)",

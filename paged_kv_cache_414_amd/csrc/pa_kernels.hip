@@ -787,7 +787,7 @@ constexpr int kPrefixSlots = kPrefixWaves > 4 ? kPrefixWaves / 2 : kPrefixWaves;
 constexpr int kPrefixThreads = kPrefixWaves * kWave;
 static_assert(kPrefixWaves == kPrefixSlots || kPrefixWaves == 2 * kPrefixSlots, "prefix waves");
 
-// One lane's run of kN fp16 values of a V row (kN = D / 16: 8, 12, 16 or 32 bytes).
+// One lane's run of kN fp16 values of a V row (kN = D / 16: 8, 10, 12, 16 or 32 bytes).
 template <int kN> struct HalfRun;
 template <> struct HalfRun<8> {
   u32x4 w;
@@ -812,6 +812,26 @@ template <> struct HalfRun<6> {
   }
   __device__ __forceinline__ _Float16 at(int i) const { return as_h2(w[i / 2])[i % 2]; }
 };
+template <> struct HalfRun<5> {
+  // 10 bytes per lane, 2-byte aligned: the three aligned dwords around the run are read
+  // (never past the end of the row: a run that starts on an odd half ends on its last
+  // half, one that starts on an even half is followed by at least one more of the row)
+  uint32_t w[3];
+  int skip;  // 1 when the run starts on the second half of its first dword
+  __device__ __forceinline__ void load(const _Float16* p) {
+    skip = static_cast<int>((reinterpret_cast<uintptr_t>(p) >> 1) & 1);
+    const uint32_t* u = reinterpret_cast<const uint32_t*>(p - skip);
+    w[0] = __builtin_nontemporal_load(u);
+    w[1] = __builtin_nontemporal_load(u + 1);
+    w[2] = __builtin_nontemporal_load(u + 2);
+  }
+  // i is a constant after unrolling: both candidates are fixed register halves
+  __device__ __forceinline__ _Float16 at(int i) const {
+    const _Float16 here = as_h2(w[i / 2])[i % 2];
+    const _Float16 next = as_h2(w[(i + 1) / 2])[(i + 1) % 2];
+    return skip ? next : here;
+  }
+};
 template <> struct HalfRun<4> {
   u32x2 w;
   __device__ __forceinline__ void load(const _Float16* p) {
@@ -822,7 +842,8 @@ template <> struct HalfRun<4> {
 
 template <int D, int BS>
 __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int part, int head, int zz) {
-  static_assert((BS % kTile == 0 || BS == kTile / 2) && (D == 64 || D == 96 || D == 128 || D == 256), "shape");
+  static_assert((BS % kTile == 0 || BS == kTile / 2) && (D == 64 || D == 80 || D == 96 || D == 128 || D == 256),
+                "shape");
   // a tile lies in one block (kTilesPerBlock tiles per block), or with blocks of 8 tokens
   // spans two (its first 8 token rows in block 2t of the table, the last 8 in block 2t + 1)
   constexpr int kBlocksPerTile = BS < kTile ? kTile / BS : 1;
@@ -830,9 +851,13 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
   auto table_index = [](int tile, int k) { return kBlocksPerTile == 1 ? tile / kTilesPerBlock : 2 * tile + k; };
   // score product: step c (of kQLoads) gives lane group j the dims
   // [32c + 8j, 32c + 8j + 8) of its K row and query -- one 16-byte load each, and the
-  // four lane groups of a row read 64 contiguous bytes per load instruction
-  constexpr int kQLoads = D / 32;
+  // four lane groups of a row read 64 contiguous bytes per load instruction.  At D 80
+  // the last step's dims 80-95 are zero on both sides (no load reads them), and the
+  // tile's K (16 x D elements) is kQLoads loads of 512 elements, the last one partial.
+  constexpr int kQLoads = (D + 31) / 32;
+  constexpr bool kPartial = D % 32 != 0;
   constexpr int kDv = D / 16;         // dims per lane per V row, also value-product tiles
+  auto k_elem_live = [](int e) { return !kPartial || e < kTile * D; };  // element e of a tile
 
   const int grp = zz / prm.query_tiles;
   const int qtile = zz % prm.query_tiles;  // first tile of 16 queries of this workgroup
@@ -840,6 +865,7 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
   const int lane = threadIdx.x % kWave;
   const int c16 = lane % kTile;  // K row and query column of this lane
   const int j = lane / kTile;    // lane group
+  auto dims_live = [j](int c) { return !kPartial || 32 * c + 8 * j < D; };  // step c, this lane
 
   const int s0 = prm.group_starts[grp];
   const int n_seqs = prm.group_starts[grp + 1] - s0;
@@ -857,7 +883,7 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
       const _Float16* qp = static_cast<const _Float16*>(prm.query) +
                            (static_cast<size_t>(s0 + q0 + c16) * prm.num_heads + head) * D + 8 * j;
 #pragma unroll
-      for (int i = 0; i < kQLoads; ++i) qv[i] = load16(qp + 32 * i);
+      for (int i = 0; i < kQLoads; ++i) qv[i] = dims_live(i) ? load16(qp + 32 * i) : u32x4{0u, 0u, 0u, 0u};
     } else {
 #pragma unroll
       for (int i = 0; i < kQLoads; ++i) qv[i] = u32x4{0u, 0u, 0u, 0u};
@@ -926,12 +952,14 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
 #pragma unroll
       for (int c = 0; c < kQLoads; ++c) {
         const int e = 512 * c + 8 * lane;
-        *reinterpret_cast<u32x4*>(s_k + (e / D) * kKRow + e % D) = kraw[c];
+        if (k_elem_live(e)) *reinterpret_cast<u32x4*>(s_k + (e / D) * kKRow + e % D) = kraw[c];
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int c = 0; c < kQLoads; ++c) kv[c] = *reinterpret_cast<const u32x4*>(s_k + c16 * kKRow + 32 * c + 8 * j);
+      for (int c = 0; c < kQLoads; ++c)
+        kv[c] = dims_live(c) ? *reinterpret_cast<const u32x4*>(s_k + c16 * kKRow + 32 * c + 8 * j)
+                             : u32x4{0u, 0u, 0u, 0u};
       // scores: sc[v] = <K row 4j+v, query c16>
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -997,7 +1025,10 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
           const size_t off = static_cast<size_t>(phys) * block_stride +
                              static_cast<size_t>(tile % kTilesPerBlock) * kTile * D;
 #pragma unroll
-          for (int ii = 0; ii < kQLoads; ++ii) kv[ii] = load_kv16(k_head + off + 512 * ii + 8 * lane);
+          for (int ii = 0; ii < kQLoads; ++ii) {
+            const int e = 512 * ii + 8 * lane;
+            kv[ii] = k_elem_live(e) ? load_kv16(k_head + off + e) : u32x4{0u, 0u, 0u, 0u};
+          }
 #pragma unroll
           for (int v = 0; v < 4; ++v) vr[v].load(v_head + off + (4 * j + v) * D + kDv * c16);
         } else {
@@ -1009,7 +1040,9 @@ __device__ __forceinline__ void prefix_workgroup(const PrefixParams& prm, int pa
 #pragma unroll
           for (int ii = 0; ii < kQLoads; ++ii) {
             const int e = 512 * ii + 8 * lane;
-            kv[ii] = e < 8 * D ? load_kv16(k_head + off0 + e) : load_kv16(k_head + off1 + (e - 8 * D));
+            kv[ii] = !k_elem_live(e) ? u32x4{0u, 0u, 0u, 0u}
+                     : e < 8 * D     ? load_kv16(k_head + off0 + e)
+                                     : load_kv16(k_head + off1 + (e - 8 * D));
           }
           const size_t off_v = j < 2 ? off0 : off1;  // rows 4j .. 4j + 3
 #pragma unroll
@@ -1322,6 +1355,7 @@ hipError_t launch_decode_shared_fused(const PrefixParams& pp, const DecodeParams
                                       hipStream_t stream) {
   switch (head_dim) {
     case 64: return launch_fused_d<64>(pp, dp, block_size, stream);
+    case 80: return launch_fused_d<80>(pp, dp, block_size, stream);
     case 96: return launch_fused_d<96>(pp, dp, block_size, stream);
     case 128: return launch_fused_d<128>(pp, dp, block_size, stream);
     case 256: return launch_fused_d<256>(pp, dp, block_size, stream);
@@ -1334,6 +1368,7 @@ hipError_t launch_decode_prefix(const PrefixParams& prm, int head_dim, int block
                                 hipStream_t stream) {
   switch (head_dim) {
     case 64: return launch_prefix_d<64>(prm, block_size, stream);
+    case 80: return launch_prefix_d<80>(prm, block_size, stream);
     case 96: return launch_prefix_d<96>(prm, block_size, stream);
     case 128: return launch_prefix_d<128>(prm, block_size, stream);
     case 256: return launch_prefix_d<256>(prm, block_size, stream);

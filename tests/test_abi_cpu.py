@@ -182,7 +182,7 @@ def _bad_shared(ops, **over):
 @pytest.mark.parametrize("over,status", [
     (dict(dtype=0), 3),            # fp32 is not built for the shared-prefix decode
     (dict(bs=4), 3),
-    (dict(D=80), 3),
+    (dict(D=72), 3),
     (dict(maxp=40), 2),            # not a whole number of blocks
     (dict(maxp=-16), 2),
     (dict(maxs=-1), 2),
@@ -244,10 +244,10 @@ def test_shared_prefix_planning(ops):
     assert prefix_slots(1, 0, 1024) == 2        # 0: the average group (64 members) decides
     assert prefix_slots(2, 0, 1024) == 2        # average 32 members: 2 x 2 x 32 = 128
     assert prefix_slots(1, 128, 512) == 1       # 8 tiles x 32 = 256 already
-    # head dims 64, 96, 128 and 256 are built for the shared-prefix decode; others are refused
-    for dd in (64, 96, 256):
+    # head dims 64, 80, 96, 128 and 256 are built for the shared-prefix decode; others are refused
+    for dd in (64, 80, 96, 256):
         assert ops.pa_decode_shared_prefix_workspace_bytes(s, h, dd, 16, 8, 1024, 272) > 0
-    for dd in (80, 72):
+    for dd in (72, 112):
         assert ops.lib.pa_decode_shared_prefix_workspace_bytes(s, h, dd, 16, 8, 0, 1024, 272, 0, 0) == 0
         assert b"head_dim" in ops.lib.pa_last_error()
     # blocks of 8 tokens: the pass after the prefix is planned for 8 more tokens (a prefix

@@ -77,6 +77,9 @@ CASES = [
     ("bs8_d256", 256, 8, [6, 6], (2, 5), (0, 30), 0, 0, 16),
     ("d96", 96, 16, [8, 3, 20], (1, 5), (0, 80), 1, 0, 0),
     ("d96_bs8", 96, 8, [5, 9], (3, 13), (1, 60), 0, 0, 32),
+    ("d80", 80, 16, [8, 4, 17], (1, 5), (0, 70), 2, 0, 0),
+    ("d80_bs8", 80, 8, [6, 3], (3, 11), (1, 50), 1, 0, 16),
+    ("d80_bs32", 80, 32, [9, 2], (1, 4), (1, 90), 0, 64, 32),
 ]
 
 
@@ -115,7 +118,7 @@ def test_prefix_partition_sizes_agree():
         assert max_abs_err(run_shared(b, 0, pp), want) <= TOL, pp
 
 
-@pytest.mark.parametrize("head_dim,block_size", [(64, 16), (256, 16), (128, 8), (96, 8)])
+@pytest.mark.parametrize("head_dim,block_size", [(64, 16), (256, 16), (128, 8), (96, 8), (80, 16)])
 def test_prefix_states_match_oracle(head_dim, block_size):
     """Prefix slots of the workspace (base-2 m, l, o) against the oracle's partition
     states over the same prefix token ranges: m2 = m * log2(e).  The prefix pass reads
@@ -291,15 +294,18 @@ def test_random_shared_prefix_layouts_block_size_8(i):
     assert max_abs_err(got, _oracle(b)) <= TOL, i
 
 
+@pytest.mark.parametrize("head_dim", [80, 96])
 @pytest.mark.parametrize("i", range(8))
-def test_random_shared_prefix_layouts_head_dim_96(i):
-    """Random layouts at head dim 96 (3 score steps and 6 value tiles per wave, V runs of
-    12 bytes per lane), block sizes 8 to 256."""
-    _, bs, sizes, (plo, phi), (slo, shi), ungrouped, part, ppart, mgs = _draw_shared_case(300 + i)
+def test_random_shared_prefix_layouts_head_dim_80_96(head_dim, i):
+    """Random layouts at head dims 80 (a partial third score step, 10-byte V runs per
+    lane) and 96 (3 score steps, 12-byte V runs), block sizes 8 to 256."""
+    _, bs, sizes, (plo, phi), (slo, shi), ungrouped, part, ppart, mgs = _draw_shared_case(
+        300 + i + 50 * (head_dim == 80))
     if i % 2:  # every other case with blocks of 8 tokens
         bs, part = 8, 0
-    b = workloads.make_shared_prefix_batch(f"random96_{i}", seed=6000 + i, group_sizes=sizes,
-                                           num_heads=2, head_dim=96, block_size=bs,
+    b = workloads.make_shared_prefix_batch(f"random{head_dim}_{i}", seed=6000 + head_dim + i,
+                                           group_sizes=sizes,
+                                           num_heads=2, head_dim=head_dim, block_size=bs,
                                            prefix_blocks_low=plo, prefix_blocks_high=phi,
                                            suffix_low=slo, suffix_high=shi, ungrouped=ungrouped,
                                            pool_slack=1.3)

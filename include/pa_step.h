@@ -72,7 +72,9 @@ typedef struct pa_step_config {
   int32_t max_seqs;            /* running sequences per step, > 0 */
   int32_t max_blocks_per_seq;  /* block-table width, > 0 */
   int32_t max_admit_tokens;    /* prompt tokens requested per step, >= 0 */
-  int32_t max_groups;          /* shared-prefix groups per step, >= 0 (0: never) */
+  int32_t max_groups;          /* shared-prefix groups per step, >= 0 (0: never); > 0
+                                  only with PA_F16 pools (the shared-prefix decode),
+                                  else pa_step_create fails with PA_ERR_UNSUPPORTED */
 } pa_step_config;
 
 /* New executor over the manager `bm` and the device pools key_cache / value_cache
@@ -96,8 +98,8 @@ typedef struct pa_step_args {
   /* Shared-prefix groups (NULL and 0: the decode is pa_decode).  Host array: rows
    * group_starts[g] .. group_starts[g + 1] - 1 form group g; group_starts[0] = 0,
    * group_starts[num_groups] = num_seqs, non-decreasing; num_groups <= max_groups.
-   * Only for what pa_decode_shared_prefix supports (fp16, D 64 or 128, block size
-   * 16 to 256). */
+   * The executor was created with max_groups > 0, so the pools are fp16, which
+   * pa_decode_shared_prefix supports at every head dim and block size. */
   const int32_t* group_starts;
   int32_t num_groups;
   /* Sequences that finish with this step (host, distinct known ids; they may be

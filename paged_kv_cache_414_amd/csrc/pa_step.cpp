@@ -147,6 +147,11 @@ pa_step_engine* pa_step_create(pa_block_manager* bm, const pa_step_config* confi
                   c.num_heads, c.max_seqs, c.max_blocks_per_seq, c.max_admit_tokens, c.max_groups);
     return nullptr;
   }
+  if (c.max_groups > 0 && c.dtype != PA_F16) {
+    // the shared-prefix decode is built for fp16; refused here, not halfway through a step
+    pa::set_error(PA_ERR_UNSUPPORTED, "max_groups %d needs PA_F16 pools (the shared-prefix decode)", c.max_groups);
+    return nullptr;
+  }
   if (static_cast<int64_t>(c.max_blocks_per_seq) * bs > INT32_MAX) {
     pa::set_error(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size exceeds the int32 range");
     return nullptr;

@@ -54,7 +54,8 @@ def test_create_rejects_bad_configurations():
     assert b"NULL" in lib.pa_last_error()
     for kw, text in (({"head_dim": 72}, b"head_dim"), ({"dtype": 5}, b"dtype"),
                      ({"max_seqs": 0}, b"max_seqs"), ({"max_groups": -1}, b"max_groups"),
-                     ({"max_admit_tokens": -3}, b"max_admit_tokens")):
+                     ({"max_admit_tokens": -3}, b"max_admit_tokens"),
+                     ({"max_groups": 2, "dtype": 0}, b"PA_F16")):  # groups need fp16 pools
         assert not lib.pa_step_create(bm._h, ctypes.byref(_config(engine, **kw)), fake, fake)
         assert text in lib.pa_last_error(), kw
     odd = blocks.BlockManager(64, 24)  # a block size pa_decode is not built for

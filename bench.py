@@ -655,7 +655,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode path shards by sequence or head with no exchange, see the design notes)",
+              "(across GPUs the decode path would shard by sequence or by head, with no exchange "
+              "between them)",
               file=sys.stderr)
         sys.exit(2)
 

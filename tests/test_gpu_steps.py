@@ -37,7 +37,7 @@ def rotating_rows(step, num_seqs, count):
 
 def replay(mix, decode_steps, pool_steps, rotate=0):
     """Replay every step through the oracle.  Decode outputs: the whole batch at
-    `decode_steps`, and `rotate` rows chosen by rotating_rows at every other step."""
+    `decode_steps`, and `rotate` rows chosen by rotating_rows at each of the other steps."""
     spec = mix.spec
     shape = (spec.num_blocks, spec.num_heads, spec.block_size, spec.head_dim)
     k_pool = np.zeros(shape, dtype=spec.dtype)

@@ -39,6 +39,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #ifndef PA_KV_LOADS_IN_FLIGHT
 #define PA_KV_LOADS_IN_FLIGHT 8  // 16-byte K+V loads per lane issued before their use
 #endif
+#ifndef PA_KV_LOADS_IN_FLIGHT_WIDE
+#define PA_KV_LOADS_IN_FLIGHT_WIDE 16  // the same for the 16-wave decode workgroups
+#endif
 #ifndef PA_NONTEMPORAL_KV
 #define PA_NONTEMPORAL_KV 1  // 1: K/V loads carry the non-temporal (streaming) hint
 #endif
@@ -207,9 +210,11 @@ struct Geometry {
       BS < kTokPerLoad * PA_MAX_LOADS_PER_UNIT ? BS : kTokPerLoad * PA_MAX_LOADS_PER_UNIT;
   static constexpr int kUnitsPerBlock = BS / kUnitTok;
   static constexpr int kLoads = kUnitTok / kTokPerLoad;    // loads per unit (K, and V)
-  // units fetched together per wave: PA_KV_LOADS_IN_FLIGHT 16-byte loads per lane
-  static constexpr int kUnroll =
-      2 * kLoads >= PA_KV_LOADS_IN_FLIGHT ? 1 : PA_KV_LOADS_IN_FLIGHT / (2 * kLoads);
+  // whole units a wave fetches together, all their loads issued before the first fold,
+  // for `in_flight` 16-byte K+V loads per lane (at least one unit)
+  static constexpr int units_in_flight(int in_flight) {
+    return 2 * kLoads >= in_flight ? 1 : in_flight / (2 * kLoads);
+  }
   // Heads of one block a wave may fold as one unit (PA_HEADS_PER_UNIT): the chunks of
   // adjacent heads are adjacent in the pool, so two 4 KiB chunks are one contiguous
   // 8 KiB run per unit of K (and of V), the run a 32-token block of one head gives.
@@ -332,7 +337,15 @@ __device__ __forceinline__ void attend_units(RowState<Geometry<T, D, BS>::kVec> 
   static_assert(HU == 1 || G::kUnitsPerBlock == 1, "heads share a unit only when the unit is the block");
   constexpr int kL = HU * G::kLoads;  // loads per unit of K (and of V)
   constexpr int kUnitBytes = HU * G::kUnitTok * D * static_cast<int>(sizeof(T));
-  constexpr int kUnroll = HU == 1 ? G::kUnroll : 1;
+  // Loads in flight per lane: 8 in the 8-wave workgroups, 16 in the 16-wave ones (two
+  // 8-load units at block size 16, fp16 D 128).  The 16-wave instance holds one workgroup
+  // per CU at either depth (74 or 89 VGPRs), and the deeper one streams 0.6-1.1 % faster
+  // on batches of 96 and 256 sequences U[300, 2048] (fp16; block size 8 and 16, D 96 and
+  // 128) and 1.8 % at D 64 with blocks of 32, the same on short contexts (MI355X, same
+  // box, interleaved builds); in the 8-wave instance the extra registers would cost a
+  // third of its workgroups per CU.  The fold order is the same, so are the results.
+  constexpr int kInFlight = W == kWavesWide ? PA_KV_LOADS_IN_FLIGHT_WIDE : PA_KV_LOADS_IN_FLIGHT;
+  constexpr int kUnroll = HU == 1 ? G::units_in_flight(kInFlight) : 1;
   // element offset of this lane's load i in a unit: head i / kLoads, rows (i % kLoads)
   auto elem = [&](int i) {
     return (i / G::kLoads) * (BS * D) + (i % G::kLoads) * G::kTokPerLoad * D + lane_off;

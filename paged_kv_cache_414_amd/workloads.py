@@ -162,8 +162,8 @@ def make_static_batch(name: str, *, seed: int, num_seqs: int, num_heads: int,
     rng = np.random.default_rng(seed)
     ctx = rng.integers(ctx_low, ctx_high + 1, size=num_seqs).astype(np.int32)
     needed = int(sum(-(-int(c) // block_size) for c in ctx))
-    if num_blocks is None:
-        num_blocks = int(math.ceil(pool_slack * needed))
+    if num_blocks is None:  # at least one block, for the table padding of empty contexts
+        num_blocks = max(1, int(math.ceil(pool_slack * needed)))
     if needed > num_blocks:
         raise ValueError(f"{name}: {needed} blocks needed, pool has {num_blocks}")
     if max_blocks_per_seq is None:

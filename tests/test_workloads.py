@@ -104,3 +104,13 @@ def test_shared_prefix_prompt_lengths():
     lens = d.prompt_lens()
     assert lens.shape == (8,)
     assert np.all((lens >= 1025) & (lens <= 1039))
+
+
+def test_batch_of_empty_contexts_gets_a_one_block_pool():
+    """Every context 0: no block is live, the pool still holds the one (poisoned) block the
+    table padding points at."""
+    b = workloads.make_static_batch("empty", seed=5, num_seqs=3, num_heads=2, head_dim=64,
+                                    block_size=16, ctx_low=0, ctx_high=0, dtype=np.float16)
+    assert b.num_blocks == 1 and b.k_pool.shape[0] == 1
+    assert np.all(b.context_lens == 0) and np.all(b.block_tables == 0)
+    assert np.all(np.isnan(b.k_pool)) and np.all(np.isnan(b.v_pool))

@@ -187,6 +187,26 @@ def test_shared_prefix_full_batch_matches_oracle_and_pa_decode():
     assert max_abs_err(got, plain.astype(np.float64)) <= 2 * TOL
 
 
+@pytest.mark.parametrize("sizes,prefix_tokens,hd,bs", [
+    ([8] * 8, 1032, 128, 8), ([8] * 8, 1024, 256, 16), ([64], 2048, 128, 16)],
+    ids=["8x8_bs8", "8x8_d256", "1x64"])
+def test_benchmark_group_layouts_match_oracle(sizes, prefix_tokens, hd, bs):
+    """The larger group layouts the benchmark times (32 heads, 200-330 own tokens per
+    member), at full size: the passes after the prefix and pa_decode on them run 16-wave
+    workgroups. Every output of both calls against the oracle."""
+    from tests.gpu_util import DeviceBatch
+    b = workloads.make_shared_prefix_batch("groups", seed=3, group_sizes=sizes, num_heads=32,
+                                           head_dim=hd, block_size=bs,
+                                           prefix_blocks_low=prefix_tokens // bs,
+                                           prefix_blocks_high=prefix_tokens // bs,
+                                           suffix_low=200, suffix_high=330)
+    want = _oracle(b)
+    got = run_shared(b, max_group_size=max(sizes))
+    assert np.all(np.isfinite(got))
+    assert max_abs_err(got, want) <= TOL
+    assert max_abs_err(DeviceBatch(b).decode().astype(np.float64), want) <= TOL
+
+
 def test_more_than_64_prefix_tiles_per_wave():
     """One prefix partition of 9,000+ shared tokens: each of the 8 waves folds more than
     64 tiles, so the tiles' block ids are fetched in several chunks."""
